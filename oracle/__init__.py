@@ -1,0 +1,46 @@
+"""Plain, slow CPU oracle of the one-pass typed-decision scoring hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link this
+package: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` use it. It shares no code with the HIP library (no kernels, headers, tables or
+helpers); both sides are fed the same seeded inputs from ``synth``.
+
+It follows the blink.py page (thegovind/blink-4b):
+  * ``pack``      -- the ragged right-padded packer ("torch engine" section: _batches, _padded,
+                     and the batch loop of _forward / _forward_shared);
+  * ``attention`` -- causal attention of each question's tail over one shared prefix, computed
+                     as the plain full-sequence definition and, independently, as a prefix
+                     partial merged with a tail partial ("torch engine" section: _forward_shared;
+                     PREFIX_CACHE comment in "constants the deployment sets");
+  * ``readout``   -- last-valid-row gather, FP64 dot against the offered labels' unembedding
+                     rows, temperature softmax and first-index argmax ("torch engine" section:
+                     _read; "answer assembly" section: softmax and answer_for).
+
+Arithmetic is float64 throughout; bf16 inputs are widened exactly.
+Every function is pinned by tests under ``tests/test_oracle_*.py``; none is "parity unpinned".
+"""
+
+from .pack import pack_ragged, MAX_QUESTIONS, MAX_INPUT_TOKENS, TOKEN_BUDGET
+from .attention import (
+    bf16_to_f64,
+    attention_full,
+    attention_decomposed,
+    attention_rows,
+)
+from .readout import label_readout, softmax_t, MAX_OPTIONS
+from .path import score_request
+
+__all__ = [
+    "pack_ragged",
+    "MAX_QUESTIONS",
+    "MAX_INPUT_TOKENS",
+    "TOKEN_BUDGET",
+    "MAX_OPTIONS",
+    "bf16_to_f64",
+    "attention_full",
+    "attention_decomposed",
+    "attention_rows",
+    "label_readout",
+    "softmax_t",
+    "score_request",
+]
