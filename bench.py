@@ -1,0 +1,200 @@
+"""Benchmark of one-pass typed-decision scoring on one MI355X.
+
+A step is the whole hot path over one request: host pack of the question tails, upload of the
+row tables, shared-prefix tail-prefill attention (HIP), label readout (HIP), and the copy of the
+label probabilities and argmax back to the host. Inputs stay resident in HBM between steps.
+
+Default workload: the 4B-like layer slice (32 query / 8 KV heads, head_dim 128, a 2048-token
+shared prefix, 32 questions with 64-256-token tails, readout over vocab 151936 x hidden 2560 with
+2-8 options per question, temperature 1.0), synthetic seeded data.
+
+Prints ONE JSON line (see the "metric" key). The dominant kernel's roofline figure uses HIP
+events recorded on the launch stream around every timed attention launch; the CPU baseline is
+the FP64 oracle timed on a bounded sample of the same request.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+
+
+def attention_flops(cfg, tail_len) -> float:
+    n = np.asarray(tail_len, np.float64)
+    return float(4.0 * cfg.head_dim * cfg.n_heads_q * np.sum(n * cfg.prefix_len + n * (n + 1) / 2))
+
+
+def attention_bytes(cfg, tail_len) -> float:
+    valid = float(np.sum(tail_len))
+    d = cfg.head_dim
+    return (valid * (cfg.n_heads_q + 2 * cfg.n_heads_kv) * d * 2
+            + cfg.prefix_len * 2 * cfg.n_heads_kv * d * 2 + valid * cfg.n_heads_q * d * 2)
+
+
+def readout_bytes(cfg, cand_ids, n) -> float:
+    distinct = np.unique(cand_ids).shape[0]
+    return float(distinct * cfg.d_model * 2 + n * cfg.d_model * 2 + len(cand_ids) * 12 + 4 * n)
+
+
+def cpu_baseline(cfg, req_tables, tensors, budget_s: float):
+    """The oracle (as it stands) on whole questions of the same request until ~budget_s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle.path import score_request
+
+    n = len(req_tables.tail_len)
+    done, t0 = 0, time.perf_counter()
+    while True:  # whole questions, cycling through the request, until the time budget is used
+        score_request(req_tables.tail_len, tensors, req_tables.cand_ids, req_tables.cand_off, cfg,
+                      questions=[done % n])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": done / elapsed,
+        "unit": "questions/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} questions (cycling over the request's {n}) scored whole (pack, all "
+                  f"{cfg.n_heads_q} heads of attention, readout) in {elapsed:.1f} s, float64 numpy "
+                  f"on {len(os.sched_getaffinity(0))} host cores",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload number (1-5)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the scoring path "
+              "runs on a single device)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(args.config)
+    rng = synth.rng_for(cfg)
+    tables = synth.draw_tables(cfg, rng)
+    pk = blink.pack_ragged(tables.tail_len, cfg.prefix_len, cfg.token_budget, cfg.max_rows)
+    host = synth.draw_tensors(cfg, rng, pk.total_padded_tokens)
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    tensors = {k: dev(v) for k, v in host.items() if v.size}
+    if cfg.prefix_len == 0:
+        tensors.pop("k_prefix", None)
+        tensors.pop("v_prefix", None)
+    stream = torch.cuda.current_stream()
+    step = blink.ScoringStep(tables.tail_len, tables.cand_ids, tables.cand_off, tensors,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        p = step.pack_and_upload()
+        ev[i][0].record(stream)
+        step.attention(p)
+        ev[i][1].record(stream)
+        step.readout()
+        ev[i][2].record(stream)
+        with torch.cuda.stream(stream):
+            step.h_probs.copy_(step.probs, non_blocking=True)
+            step.h_argmax.copy_(step.argmax, non_blocking=True)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    read_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    flops = attention_flops(cfg, tables.tail_len)
+    abytes = attention_bytes(cfg, tables.tail_len)
+    rbytes = readout_bytes(cfg, tables.cand_ids, cfg.n_questions)
+    n = cfg.n_questions
+    ms_per_step = elapsed * 1e3 / args.steps
+    if cfg.prefix_len > 0:
+        achieved = flops / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": "prefix_tail_attention_kernel",
+                "work_per_launch": f"{flops:.4e} FLOP"}
+    else:
+        achieved = abytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                "kernel": "prefix_tail_attention_kernel",
+                "work_per_launch": f"{abytes:.4e} B"}
+
+    baseline = None
+    if not args.no_cpu_baseline:
+        baseline = cpu_baseline(cfg, tables, host, args.cpu_budget)
+
+    line = {
+        "metric": "scored questions/s (one request = pack + tail-prefix attention + label readout)",
+        "value": n * args.steps / elapsed,
+        "unit": "questions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name} (config {cfg.number}): {cfg.n_heads_q} q / {cfg.n_heads_kv} kv "
+                        f"heads, head_dim {cfg.head_dim}, prefix {cfg.prefix_len}, {n} questions "
+                        f"with tails {cfg.tail_lo}-{cfg.tail_hi}, hidden {cfg.d_model}, vocab "
+                        f"{cfg.vocab}, options {cfg.k_lo}-{cfg.k_hi}, T {cfg.temperature}",
+            "questions": n,
+            "valid_tail_tokens": int(np.sum(tables.tail_len)),
+            "padded_tokens": pk.total_padded_tokens,
+            "batches": pk.n_batches,
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "kernels": {
+            "attention_ms": attn_ms,
+            "attention_tflops": flops / (attn_ms * 1e-3) / 1e12,
+            "attention_mfma_frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "readout_ms": read_ms,
+            "readout_gbps": rbytes / (read_ms * 1e-3) / 1e9,
+            "readout_hbm_frac": rbytes / (read_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "readout_algorithmic_bytes": rbytes,
+        },
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * blink.h -- C ABI of the one-pass typed-decision scoring hot path on MI355X (gfx950).
+ *
+ * The method (blink.py page, thegovind/blink-4b, module docstring and "torch engine"
+ * section): every question of a request is run as a right-padded prefill that generates no
+ * token; question tails are packed into batches under a padded-token budget; with the shared
+ * prefix opt-in, the prefix (system prompt plus evidence) is encoded once and every tail
+ * attends to it; each question's answer is the next-token distribution over its offered
+ * option labels, read from the hidden row of its last real token.
+ *
+ * Request model: one shared prefix of P >= 0 tokens plus 1..512 questions. A question has its
+ * own tail of n_i >= 1 tokens (P + n_i <= 131072) and 1..255 options; option k is the label
+ * A..Z, AA..ZZ with index k and maps to one token id, i.e. one unembedding row.
+ *
+ * Conventions shared by every entry point:
+ *  - Return value: BLINK_OK (0) or a negative BLINK_E_* code. On error, blink_last_error()
+ *    returns a message for the calling thread (the text stays valid until that thread's next
+ *    call into the library); on success it returns "".
+ *  - Every argument error is detected before anything is launched; a call that fails
+ *    validation has no effect on device memory.
+ *  - The caller owns all memory and the stream. The library allocates no device memory,
+ *    keeps no global state between calls and may be called from several threads.
+ *  - Device entry points are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream). Device arrays must stay alive until the work on `stream` has finished.
+ *  - bf16 means the 16-bit brain-float storage format. All tensors are dense and row-major
+ *    with the last dimension contiguous; device tensors must be 16-byte aligned.
+ *  - Tables that live on the device (offsets, ids) are read by the kernels without host
+ *    checks. The kernels never access memory outside the sizes passed in, whatever the table
+ *    contents: a malformed entry makes that question's outputs NaN / -1 (readout) or leaves
+ *    its attention rows unwritten.
+ */
+#ifndef BLINK_H
+#define BLINK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLINK_OK 0
+#define BLINK_E_INVALID (-1) /* malformed argument: null pointer, bad size, bad alignment */
+#define BLINK_E_LIMIT (-2)   /* a limit of the method is exceeded (questions, options, context) */
+#define BLINK_E_DEVICE (-3)  /* the HIP runtime refused a launch */
+
+/* Limits of the method ("constants the deployment sets" section of the blink.py page). */
+#define BLINK_MAX_QUESTIONS 512
+#define BLINK_MAX_OPTIONS 255
+#define BLINK_MAX_INPUT_TOKENS 131072
+#define BLINK_TOKEN_BUDGET 32768
+
+/* Message for the calling thread's last failed call; "" after a successful call. */
+const char *blink_last_error(void);
+
+/* ABI version of this header (incremented on any signature change). */
+int blink_abi_version(void);
+#define BLINK_ABI_VERSION 1
+
+/*
+ * blink_pack_ragged -- host, synchronous, integer only.
+ *
+ * Packs question tails into right-padded batches ("torch engine" section: _batches and
+ * _padded, and the tail loop of _forward_shared). Questions are visited in ascending tail
+ * length, equal lengths in question order. A question joins the current batch unless the
+ * batch's padded size with it (widest row times rows, newcomer included) would exceed
+ * `token_budget`, or the batch already holds `max_rows` rows (max_rows > 0); otherwise it
+ * opens a new batch, so a question longer than the budget runs alone. A batch's width is its
+ * longest tail; rows are left-aligned. Batches are laid end to end in visiting order in one
+ * token-major buffer of `*total_padded_tokens` tokens (this single-buffer layout is this
+ * library's reading; the pages keep one tensor per forward).
+ *
+ * Inputs (host):
+ *   tail_len[n]       tokens of each question's own tail, >= 1
+ *   n_questions       1..512                          (else BLINK_E_LIMIT)
+ *   prefix_len        P >= 0; only checks P + tail_len[i] <= 131072 (else BLINK_E_LIMIT,
+ *                     message names the question and "the maximum context length")
+ *   token_budget      >= 1 (the pages use 32768)
+ *   max_rows          0 = no row cap, else rows per batch at most max_rows
+ * Outputs (host arrays the caller allocates; any may not be NULL):
+ *   order[n]          questions in visiting order
+ *   batch_of[n], row_of[n]      batch and row of each question
+ *   token_offset[n]   first token of the question's row in the packed buffer
+ *   last_row[n]       token index of the question's last real token (its readout row)
+ *   valid_start[n+1]  exclusive prefix sum of tail_len in question order (valid_start[n] =
+ *                     total real tokens); this is the row table the attention call takes
+ *   batch_first[n+1]  start of each batch in order[]; entries past n_batches are unspecified
+ *   batch_width[n]    padded width of each batch
+ *   batch_base[n+1]   first token of each batch; batch_base[n_batches] = total padded tokens
+ *   n_batches, total_padded_tokens, total_valid_tokens (scalars)
+ */
+int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, int32_t prefix_len,
+                      int64_t token_budget, int32_t max_rows,
+                      int32_t *order, int32_t *batch_of, int32_t *row_of,
+                      int64_t *token_offset, int64_t *last_row, int32_t *valid_start,
+                      int32_t *batch_first, int32_t *batch_width, int64_t *batch_base,
+                      int32_t *n_batches, int64_t *total_padded_tokens,
+                      int64_t *total_valid_tokens);
+
+/*
+ * blink_prefix_tail_attention -- device, asynchronous.
+ *
+ * Shared-prefix tail-prefill attention ("torch engine" section, _forward_shared; the
+ * PREFIX_CACHE comment in "constants the deployment sets"). For question i, query head h
+ * and tail position t < n_i:
+ *     out[tok, h, :] = sum_j w_j v_j / sum_j w_j,  w_j = exp(scale * <q[tok,h,:], k_j> - max)
+ * over the P prefix keys of KV head g = h / (H_q / H_kv) followed by the question's own tail
+ * keys 0..t (tok = token_offset[i] + t). This equals plain causal attention over the full
+ * sequence [prefix ; tail_i] at positions P..P+n_i-1; only the floating-point order differs.
+ * Inputs are post-rotary; no positional encoding is applied. Softmax and accumulation are
+ * FP32; QK^T and PV use bf16 matrix cores; out is rounded to bf16 (nearest even).
+ *
+ *   q        bf16 [T_pad, H_q, D]     device
+ *   k_tail, v_tail  bf16 [T_pad, H_kv, D]   device
+ *   k_prefix, v_prefix bf16 [P, H_kv, D]    device; may be NULL iff prefix_len == 0
+ *   out      bf16 [T_pad, H_q, D]     device; rows of padding positions are not written
+ *   d_token_offset  int64 [n]  device: first token of question i (from blink_pack_ragged)
+ *   d_valid_start   int32 [n+1] device: exclusive prefix sum of tail lengths (question order)
+ *   n_questions       1..512
+ *   total_valid_tokens  must equal d_valid_start[n]; sizes the launch
+ *   total_padded_tokens T_pad (>= every token_offset[i] + n_i)
+ *   prefix_len        P, 0..131071
+ *   n_heads_q, n_heads_kv  H_kv >= 1, H_q % H_kv == 0, H_q / H_kv <= 16
+ *   head_dim          64 or 128
+ *   scale             finite, > 0 (1/sqrt(D) for standard attention)
+ * Rows of one question never depend on which other questions share the launch (results are
+ * bitwise identical whether a question runs alone or packed with others).
+ */
+int blink_prefix_tail_attention(const void *q, const void *k_tail, const void *v_tail,
+                                const void *k_prefix, const void *v_prefix, void *out,
+                                const int64_t *d_token_offset, const int32_t *d_valid_start,
+                                int32_t n_questions, int64_t total_valid_tokens,
+                                int64_t total_padded_tokens, int32_t prefix_len,
+                                int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                float scale, void *stream);
+
+/*
+ * blink_label_readout -- device, asynchronous.
+ *
+ * Label readout ("torch engine" section, _read; "answer assembly" section, softmax and
+ * answer_for): for question i, h = hidden[last_row[i]] widened to FP32; for each offered
+ * option k < K_i, logits[off_i + k] = sum_d W_U[cand_ids[off_i + k], d] * h[d] with FP32
+ * accumulation; probs = softmax(logits / temperature) over the question's own options;
+ * argmax[i] = the first option index with the largest logit.
+ *
+ *   hidden      bf16 [hidden_rows, d_model]  device (hidden_rows = T_pad)
+ *   d_last_row  int64 [n]   device: row of each question's last real token
+ *   w_u         bf16 [vocab, d_model]        device (unembedding / lm_head weight)
+ *   d_cand_ids  int32 [total_candidates]     device: token id of each offered label
+ *   d_cand_off  int32 [n+1] device: CSR offsets, cand_off[0] = 0, 1 <= K_i <= max_options
+ *   n_questions 1..512, total_candidates = cand_off[n] (host copy, sizes checks)
+ *   max_options 1..255: upper bound of every K_i
+ *   d_model     multiple of 8, 8..8192
+ *   temperature finite and > 0 (else BLINK_E_INVALID, "temperature must be positive")
+ *   d_logits, d_probs  float32 [total_candidates] device outputs
+ *   d_argmax    int32 [n] device output; -1 (with NaN logits/probs) marks a question whose
+ *               table entries were out of range
+ */
+int blink_label_readout(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                        const int64_t *d_last_row, const void *w_u, int64_t vocab,
+                        const int32_t *d_cand_ids, const int32_t *d_cand_off,
+                        int32_t n_questions, int64_t total_candidates, int32_t max_options,
+                        float temperature, float *d_logits, float *d_probs,
+                        int32_t *d_argmax, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLINK_H */

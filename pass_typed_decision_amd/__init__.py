@@ -1,0 +1,55 @@
+"""One-pass typed-decision scoring hot path for MI355X (gfx950).
+
+Three calls, each a thin binding of the C ABI in ``include/blink.h`` (libblink.so):
+
+* ``pack_ragged``            -- host packer: question tails into right-padded batches;
+* ``prefix_tail_attention``  -- HIP kernel: every tail attends to one cached prefix and
+                                causally to itself (bf16 MFMA, FP32 online softmax);
+* ``label_readout``          -- HIP kernel: last-real-row gather, FP32 dot with the offered
+                                labels' unembedding rows, temperature softmax, argmax.
+
+``score`` chains them for one request (the hot path of one scoring step).
+"""
+
+from ._binding import (
+    BlinkError,
+    BLINK_OK,
+    BLINK_E_INVALID,
+    BLINK_E_LIMIT,
+    BLINK_E_DEVICE,
+    EXPORTS,
+    LIBRARY,
+    MAX_INPUT_TOKENS,
+    MAX_OPTIONS,
+    MAX_QUESTIONS,
+    TOKEN_BUDGET,
+    Pack,
+    check_candidate_table,
+    label_readout,
+    load_library,
+    pack_ragged,
+    prefix_tail_attention,
+)
+from .path import ScoringStep, label_name
+
+__all__ = [
+    "BlinkError",
+    "BLINK_OK",
+    "BLINK_E_INVALID",
+    "BLINK_E_LIMIT",
+    "BLINK_E_DEVICE",
+    "EXPORTS",
+    "LIBRARY",
+    "MAX_INPUT_TOKENS",
+    "MAX_OPTIONS",
+    "MAX_QUESTIONS",
+    "TOKEN_BUDGET",
+    "Pack",
+    "check_candidate_table",
+    "label_readout",
+    "load_library",
+    "pack_ragged",
+    "prefix_tail_attention",
+    "ScoringStep",
+    "label_name",
+]

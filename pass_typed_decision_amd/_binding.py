@@ -1,0 +1,247 @@
+"""ctypes binding of libblink.so (argument marshalling only).
+
+Every computation happens in the library: the host packer in C++ and the attention and
+readout in HIP kernels for gfx950. PyTorch tensors only supply device memory and the stream.
+If the library is missing the binding raises; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libblink.so")
+
+BLINK_OK = 0
+BLINK_E_INVALID = -1
+BLINK_E_LIMIT = -2
+BLINK_E_DEVICE = -3
+MAX_QUESTIONS = 512
+MAX_OPTIONS = 255
+MAX_INPUT_TOKENS = 131072
+TOKEN_BUDGET = 32768
+
+# Every symbol declared in include/blink.h.
+EXPORTS = (
+    "blink_last_error",
+    "blink_abi_version",
+    "blink_pack_ragged",
+    "blink_prefix_tail_attention",
+    "blink_label_readout",
+)
+
+
+class BlinkError(ValueError):
+    """A call the library refused; ``code`` is the negative BLINK_E_* status."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(message)
+        self.code = code
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Loads libblink.so (once) and declares the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m pass_typed_decision_amd.build` "
+            "(the scoring path has no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    lib.blink_last_error.restype = ctypes.c_char_p
+    lib.blink_last_error.argtypes = []
+    lib.blink_abi_version.restype = ctypes.c_int
+    lib.blink_abi_version.argtypes = []
+    lib.blink_pack_ragged.restype = ctypes.c_int
+    lib.blink_pack_ragged.argtypes = [
+        _PI32, _I32, _I32, _I64, _I32,
+        _PI32, _PI32, _PI32, _PI64, _PI64, _PI32,
+        _PI32, _PI32, _PI64, _PI32, _PI64, _PI64,
+    ]
+    lib.blink_prefix_tail_attention.restype = ctypes.c_int
+    lib.blink_prefix_tail_attention.argtypes = [
+        _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _F32, _P,
+    ]
+    lib.blink_label_readout.restype = ctypes.c_int
+    lib.blink_label_readout.argtypes = [
+        _P, _I64, _I32, _P, _P, _I64, _P, _P, _I32, _I64, _I32, _F32, _P, _P, _P, _P,
+    ]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != BLINK_OK:
+        msg = load_library().blink_last_error().decode("utf-8", "replace")
+        raise BlinkError(rc, msg)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+@dataclass
+class Pack:
+    """Result of blink_pack_ragged (host arrays, question-indexed unless stated)."""
+
+    order: np.ndarray
+    batch_of: np.ndarray
+    row_of: np.ndarray
+    token_offset: np.ndarray
+    last_row: np.ndarray
+    valid_start: np.ndarray
+    batch_first: np.ndarray  # [n_batches + 1]
+    batch_width: np.ndarray  # [n_batches]
+    batch_base: np.ndarray  # [n_batches + 1]
+    n_batches: int
+    total_padded_tokens: int
+    total_valid_tokens: int
+
+
+def pack_ragged(tail_len, prefix_len: int = 0, token_budget: int = TOKEN_BUDGET,
+                max_rows: int = 0) -> Pack:
+    """Host packer (blink_pack_ragged)."""
+    lib = load_library()
+    t = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int32))
+    n = int(t.shape[0])
+    cap = max(n, 1)
+    order = np.zeros(cap, np.int32)
+    batch_of = np.zeros(cap, np.int32)
+    row_of = np.zeros(cap, np.int32)
+    token_offset = np.zeros(cap, np.int64)
+    last_row = np.zeros(cap, np.int64)
+    valid_start = np.zeros(cap + 1, np.int32)
+    batch_first = np.zeros(cap + 1, np.int32)
+    batch_width = np.zeros(cap, np.int32)
+    batch_base = np.zeros(cap + 1, np.int64)
+    nb = ctypes.c_int32(0)
+    tp = ctypes.c_int64(0)
+    tv = ctypes.c_int64(0)
+    src = t if n else np.zeros(1, np.int32)
+    _check(lib.blink_pack_ragged(
+        _ptr(src, ctypes.c_int32), n, int(prefix_len), int(token_budget), int(max_rows),
+        _ptr(order, ctypes.c_int32), _ptr(batch_of, ctypes.c_int32), _ptr(row_of, ctypes.c_int32),
+        _ptr(token_offset, ctypes.c_int64), _ptr(last_row, ctypes.c_int64),
+        _ptr(valid_start, ctypes.c_int32), _ptr(batch_first, ctypes.c_int32),
+        _ptr(batch_width, ctypes.c_int32), _ptr(batch_base, ctypes.c_int64),
+        ctypes.byref(nb), ctypes.byref(tp), ctypes.byref(tv)))
+    k = nb.value
+    return Pack(order[:n], batch_of[:n], row_of[:n], token_offset[:n], last_row[:n],
+                valid_start[:n + 1], batch_first[:k + 1], batch_width[:k], batch_base[:k + 1],
+                k, tp.value, tv.value)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise BlinkError(BLINK_E_INVALID, f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise BlinkError(BLINK_E_INVALID, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise BlinkError(BLINK_E_INVALID, f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offset,
+                          valid_start, total_valid_tokens: int, scale: float, stream=None):
+    """Launches blink_prefix_tail_attention. Shapes: q/out [T_pad, H_q, D], k/v_tail
+    [T_pad, H_kv, D], k/v_prefix [P, H_kv, D] or None; token_offset int64 [n],
+    valid_start int32 [n + 1] (device)."""
+    import torch
+
+    bf = torch.bfloat16
+    if q.dim() != 3 or k_tail.dim() != 3:
+        raise BlinkError(BLINK_E_INVALID, "q and k_tail must be [tokens, heads, head_dim]")
+    t_pad, hq, d = q.shape
+    hkv = k_tail.shape[1]
+    if tuple(k_tail.shape) != (t_pad, hkv, d) or tuple(v_tail.shape) != (t_pad, hkv, d):
+        raise BlinkError(BLINK_E_INVALID, "k_tail/v_tail must be [T_pad, H_kv, D]")
+    if tuple(out.shape) != (t_pad, hq, d):
+        raise BlinkError(BLINK_E_INVALID, "out must be [T_pad, H_q, D]")
+    p = 0 if k_prefix is None else int(k_prefix.shape[0])
+    if p:
+        if tuple(k_prefix.shape) != (p, hkv, d) or tuple(v_prefix.shape) != (p, hkv, d):
+            raise BlinkError(BLINK_E_INVALID, "k_prefix/v_prefix must be [P, H_kv, D]")
+        kp, vp = _dev(k_prefix, bf, "k_prefix"), _dev(v_prefix, bf, "v_prefix")
+    else:
+        kp = vp = ctypes.c_void_p(0)
+    n = int(token_offset.shape[0])
+    if int(valid_start.shape[0]) != n + 1:
+        raise BlinkError(BLINK_E_INVALID, "valid_start must have n + 1 entries")
+    lib = load_library()
+    _check(lib.blink_prefix_tail_attention(
+        _dev(q, bf, "q"), _dev(k_tail, bf, "k_tail"), _dev(v_tail, bf, "v_tail"), kp, vp,
+        _dev(out, bf, "out"), _dev(token_offset, torch.int64, "token_offset"),
+        _dev(valid_start, torch.int32, "valid_start"), n, int(total_valid_tokens), int(t_pad),
+        p, int(hq), int(hkv), int(d), float(scale), _stream(stream)))
+
+
+def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
+                  max_options: int, logits, probs, argmax, stream=None):
+    """Launches blink_label_readout. hidden [T_pad, d_model] bf16, last_row int64 [n],
+    w_u [vocab, d_model] bf16, cand_ids int32 [sum K], cand_off int32 [n + 1];
+    outputs logits/probs float32 [sum K], argmax int32 [n] (device)."""
+    import torch
+
+    bf = torch.bfloat16
+    if hidden.dim() != 2 or w_u.dim() != 2 or hidden.shape[1] != w_u.shape[1]:
+        raise BlinkError(BLINK_E_INVALID, "hidden and w_u must be 2-D with the same width")
+    n = int(last_row.shape[0])
+    total = int(cand_ids.shape[0])
+    if int(cand_off.shape[0]) != n + 1:
+        raise BlinkError(BLINK_E_INVALID, "cand_off must have n + 1 entries")
+    if int(logits.shape[0]) != total or int(probs.shape[0]) != total or int(argmax.shape[0]) != n:
+        raise BlinkError(BLINK_E_INVALID, "output sizes do not match the candidate table")
+    lib = load_library()
+    _check(lib.blink_label_readout(
+        _dev(hidden, bf, "hidden"), int(hidden.shape[0]), int(hidden.shape[1]),
+        _dev(last_row, torch.int64, "last_row"), _dev(w_u, bf, "w_u"), int(w_u.shape[0]),
+        _dev(cand_ids, torch.int32, "cand_ids"), _dev(cand_off, torch.int32, "cand_off"), n, total,
+        int(max_options), float(temperature), _dev(logits, torch.float32, "logits"),
+        _dev(probs, torch.float32, "probs"), _dev(argmax, torch.int32, "argmax"),
+        _stream(stream)))
+
+
+def check_candidate_table(cand_ids, cand_off, vocab: int) -> int:
+    """Host-side check of a candidate table before upload; returns max options per question.
+
+    Mirrors the pages' rules ("rendering" section: 1-255 options; "torch engine" section:
+    label token ids are distinct)."""
+    ids = np.asarray(cand_ids)
+    off = np.asarray(cand_off)
+    if off.ndim != 1 or off.shape[0] < 2 or off[0] != 0 or off[-1] != ids.shape[0]:
+        raise BlinkError(BLINK_E_INVALID, "candidate offsets must run from 0 to len(cand_ids)")
+    k = np.diff(off)
+    for i, ki in enumerate(k):
+        if not 1 <= ki <= MAX_OPTIONS:
+            raise BlinkError(BLINK_E_LIMIT, f"{int(ki)} options per choice; supported 1-{MAX_OPTIONS}")
+        row = ids[off[i]:off[i + 1]]
+        if row.min() < 0 or row.max() >= vocab:
+            raise BlinkError(BLINK_E_INVALID, f"question {i}: label token id out of range")
+        if np.unique(row).shape[0] != row.shape[0]:
+            raise BlinkError(BLINK_E_INVALID, f"question {i}: label token ids collide")
+    return int(k.max())

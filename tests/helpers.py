@@ -1,0 +1,143 @@
+"""Shared test helpers: build seeded requests, move them to the device, compare with the oracle."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from oracle.pack import pack_ragged as oracle_pack  # noqa: E402
+
+ATTN_TOL = 2e-2  # max-abs on bf16 attention outputs
+PROB_TOL = 1e-4  # max-abs on label probabilities
+LOGIT_TOL = 1e-4
+ARGMAX_GAP = 1e-5  # argmax must match exactly where the oracle's top-2 logit gap exceeds this
+
+
+class Request:
+    """One seeded request: integer tables, the oracle's pack and bf16 bit tensors."""
+
+    def __init__(self, cfg, seed=None, parts=synth.TENSOR_ORDER, tail_len=None):
+        self.cfg = cfg
+        rng = synth.rng_for(cfg, seed)
+        self.tables = synth.draw_tables(cfg, rng)
+        if tail_len is not None:
+            self.tables.tail_len = np.asarray(tail_len, np.int32)
+        self.pack = oracle_pack(self.tables.tail_len, cfg.token_budget, cfg.max_rows,
+                                cfg.prefix_len)
+        self.tensors = synth.draw_tensors(cfg, rng, self.pack["total_padded_tokens"], parts)
+
+    @property
+    def tail_len(self):
+        return self.tables.tail_len
+
+    def valid_start(self):
+        vs = np.zeros(len(self.tail_len) + 1, np.int32)
+        np.cumsum(self.tail_len, out=vs[1:])
+        return vs
+
+
+def device_bf16(bits):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def bf16_to_f32_host(t):
+    import torch
+
+    return synth.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def run_attention(req, tensors=None, token_offset=None, tail_len=None):
+    """GPU attention through the C ABI; returns the output as float32 numpy [T_pad, H_q, D]."""
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = req.cfg
+    ts = req.tensors if tensors is None else tensors
+    tail = req.tail_len if tail_len is None else np.asarray(tail_len, np.int32)
+    offs = req.pack["token_offset"] if token_offset is None else token_offset
+    q = device_bf16(ts["q"])
+    kt, vt = device_bf16(ts["k_tail"]), device_bf16(ts["v_tail"])
+    kp = vp = None
+    if cfg.prefix_len:
+        kp, vp = device_bf16(ts["k_prefix"]), device_bf16(ts["v_prefix"])
+    out = torch.full_like(q, float("nan"))
+    vs = np.zeros(len(tail) + 1, np.int32)
+    np.cumsum(tail, out=vs[1:])
+    d_off = torch.as_tensor(np.asarray(offs, np.int64)).cuda()
+    d_vs = torch.as_tensor(vs).cuda()
+    blink.prefix_tail_attention(q, kt, vt, kp, vp, out, d_off, d_vs, int(vs[-1]), cfg.scale)
+    torch.cuda.synchronize()
+    return bf16_to_f32_host(out)
+
+
+def run_readout(req, last_row=None, cand_ids=None, cand_off=None, temperature=None):
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = req.cfg
+    ids = req.tables.cand_ids if cand_ids is None else np.asarray(cand_ids, np.int32)
+    off = req.tables.cand_off if cand_off is None else np.asarray(cand_off, np.int32)
+    last = req.pack["last_row"] if last_row is None else last_row
+    t = cfg.temperature if temperature is None else temperature
+    hidden = device_bf16(req.tensors["hidden"])
+    w_u = device_bf16(req.tensors["w_u"])
+    n = len(last)
+    d_last = torch.as_tensor(np.asarray(last, np.int64)).cuda()
+    d_ids = torch.as_tensor(ids).cuda()
+    d_off = torch.as_tensor(off).cuda()
+    logits = torch.empty(len(ids), dtype=torch.float32, device="cuda")
+    probs = torch.empty_like(logits)
+    argmax = torch.empty(n, dtype=torch.int32, device="cuda")
+    kmax = int(np.diff(off).max())
+    blink.label_readout(hidden, d_last, w_u, d_ids, d_off, t, kmax, logits, probs, argmax)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), probs.cpu().numpy(), argmax.cpu().numpy()
+
+
+def valid_rows(req):
+    rows = []
+    for i, n in enumerate(req.tail_len):
+        off = req.pack["token_offset"][i]
+        rows.extend(range(off, off + int(n)))
+    return np.asarray(rows, np.int64)
+
+
+def sample_rows(req, count, seed=0):
+    """(question, position, head) samples: both ends of every tail plus random interior rows."""
+    rng = np.random.default_rng(seed)
+    cfg = req.cfg
+    picks = set()
+    for i, n in enumerate(req.tail_len):
+        for t in {0, int(n) - 1}:
+            picks.add((i, t, int(rng.integers(cfg.n_heads_q))))
+    while len(picks) < count:
+        i = int(rng.integers(len(req.tail_len)))
+        picks.add((i, int(rng.integers(req.tail_len[i])), int(rng.integers(cfg.n_heads_q))))
+    return sorted(picks)
+
+
+def check_argmax(oracle_logits, cand_off, oracle_arg, got_arg):
+    """Exact where the oracle's top-2 gap is clear; otherwise the pick must be one of the
+    (near-)tied maxima. Returns the number of near-ties seen."""
+    ties = 0
+    for i in range(len(oracle_arg)):
+        z = oracle_logits[cand_off[i]:cand_off[i + 1]]
+        top = z.max()
+        if len(z) > 1 and np.sort(z)[-2] > top - ARGMAX_GAP:
+            ties += 1
+            assert z[got_arg[i]] >= top - ARGMAX_GAP, (i, got_arg[i], oracle_arg[i])
+        else:
+            assert got_arg[i] == oracle_arg[i], (i, got_arg[i], oracle_arg[i])
+    return ties

@@ -1,0 +1,159 @@
+"""The C ABI on the host (no GPU): the library loads, exports every symbol the header
+declares, packs bit-exactly like the oracle, and refuses bad arguments before any launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from helpers import ROOT
+from oracle.pack import pack_ragged as oracle_pack
+
+HEADER = os.path.join(ROOT, "include", "blink.h")
+
+
+@pytest.fixture(scope="module")
+def blink():
+    import pass_typed_decision_amd as b
+    from pass_typed_decision_amd import build
+
+    if not os.path.exists(b.LIBRARY):
+        build.build()
+    b.load_library()
+    return b
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(blink_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(__import__("pass_typed_decision_amd").EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(blink):
+    lib = ctypes.CDLL(blink.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert blink.load_library().blink_abi_version() == 1
+
+
+def _compare(pk, ref):
+    for key in ("order", "batch_of", "row_of", "token_offset", "last_row", "batch_first",
+                "batch_width", "batch_base"):
+        np.testing.assert_array_equal(getattr(pk, key), ref[key], err_msg=key)
+    assert pk.n_batches == ref["n_batches"]
+    assert pk.total_padded_tokens == ref["total_padded_tokens"]
+    assert pk.total_valid_tokens == ref["total_valid_tokens"]
+
+
+def test_pack_matches_oracle_on_golden(blink):
+    import json
+
+    with open(os.path.join(ROOT, "tests", "golden", "pack_cases.json")) as f:
+        for case in json.load(f)["cases"]:
+            pk = blink.pack_ragged(case["tail_len"], 0, case["budget"], case["max_rows"])
+            _compare(pk, oracle_pack(case["tail_len"], case["budget"], case["max_rows"]))
+
+
+def test_pack_matches_oracle_random(blink):
+    rng = np.random.default_rng(123)
+    for _ in range(3000):
+        n = int(rng.integers(1, 513))
+        hi = int(rng.choice([3, 40, 600, 5000, 131072]))
+        lengths = rng.integers(1, hi + 1, size=n)
+        budget = int(rng.choice([1, 16, 500, 32768, 65536]))
+        max_rows = int(rng.choice([0, 0, 1, 4, 56]))
+        pk = blink.pack_ragged(lengths, 0, budget, max_rows)
+        _compare(pk, oracle_pack(lengths.tolist(), budget, max_rows))
+        vs = np.concatenate([[0], np.cumsum(lengths)])
+        np.testing.assert_array_equal(pk.valid_start, vs)
+
+
+@pytest.mark.parametrize("lengths, prefix, code, msg", [
+    ([], 0, -2, "0 questions; supported 1-512"),
+    ([1] * 513, 0, -2, "513 questions; supported 1-512"),
+    ([4, 0], 0, -1, "question 1 has an empty tail"),
+    ([5, 2], 131068, -2, "question 0 renders to 131073 tokens, over the maximum context length of 131072"),
+    ([3], -1, -1, "prefix length must be non-negative"),
+])
+def test_pack_refusals(blink, lengths, prefix, code, msg):
+    with pytest.raises(blink.BlinkError) as e:
+        blink.pack_ragged(lengths, prefix)
+    assert e.value.code == code and msg in str(e.value)
+
+
+def test_pack_limits_accepted(blink):
+    pk = blink.pack_ragged([1] * 512, 131071)
+    assert pk.n_batches == 1 and pk.total_padded_tokens == 512
+    blink.pack_ragged([4, 2], 131068)
+
+
+def _readout(lib, temperature=1.0, n=2, max_options=4, d_model=256, total=4):
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    return lib.blink_label_readout(fake, 10, d_model, fake, fake, 100, fake, fake, n, total,
+                                   max_options, temperature, fake, fake, fake, None)
+
+
+@pytest.mark.parametrize("kw, code, msg", [
+    (dict(temperature=0.0), -1, "temperature must be positive"),
+    (dict(temperature=-0.5), -1, "temperature must be positive"),
+    (dict(temperature=float("nan")), -1, "temperature must be positive"),
+    (dict(temperature=float("inf")), -1, "temperature must be positive"),
+    (dict(n=0), -2, "0 questions; supported 1-512"),
+    (dict(n=513), -2, "513 questions; supported 1-512"),
+    (dict(max_options=256), -2, "256 options per choice; supported 1-255"),
+    (dict(max_options=0), -2, "0 options per choice; supported 1-255"),
+    (dict(d_model=100), -1, "d_model 100 must be a multiple of 8"),
+    (dict(total=1), -1, "does not fit"),
+])
+def test_readout_refusals_before_launch(blink, kw, code, msg):
+    lib = blink.load_library()
+    rc = _readout(lib, **kw)
+    assert rc == code
+    assert msg in lib.blink_last_error().decode()
+
+
+def _attention(lib, n=2, total=10, t_pad=12, prefix=0, hq=4, hkv=1, d=64, scale=0.125,
+               null_prefix=True):
+    fake = ctypes.c_void_p(256)
+    pre = None if null_prefix else fake
+    return lib.blink_prefix_tail_attention(fake, fake, fake, pre, pre, fake, fake, fake, n,
+                                           total, t_pad, prefix, hq, hkv, d, scale, None)
+
+
+@pytest.mark.parametrize("kw, code, msg", [
+    (dict(n=0), -2, "0 questions; supported 1-512"),
+    (dict(d=96), -1, "head_dim 96 is not supported"),
+    (dict(hq=6, hkv=4), -1, "head counts 6/4"),
+    (dict(hq=34, hkv=2), -1, "group <= 16"),
+    (dict(scale=0.0), -1, "scale must be finite and positive"),
+    (dict(prefix=5), -1, "prefix K/V pointers are NULL"),
+    (dict(prefix=131072, null_prefix=False), -2, "maximum context length of 131072"),
+    (dict(total=20, t_pad=12), -1, "token totals do not fit"),
+    (dict(total=1), -1, "token totals do not fit"),
+])
+def test_attention_refusals_before_launch(blink, kw, code, msg):
+    lib = blink.load_library()
+    assert _attention(lib, **kw) == code
+    assert msg in lib.blink_last_error().decode()
+
+
+def test_error_text_is_cleared_by_success(blink):
+    lib = blink.load_library()
+    assert _readout(lib, temperature=0.0) == -1
+    blink.pack_ragged([3, 4])
+    assert lib.blink_last_error() == b""
+
+
+def test_label_names():
+    from pass_typed_decision_amd import label_name
+
+    assert [label_name(i) for i in (0, 1, 25, 26, 27, 51, 52, 254)] == \
+        ["A", "B", "Z", "AA", "AB", "AZ", "BA", "IU"]
+    with pytest.raises(ValueError):
+        label_name(255)

@@ -1,0 +1,127 @@
+"""GPU parity of blink_prefix_tail_attention (through the C ABI) with the FP64 oracle.
+
+Bar: max-abs 2e-2 on the bf16 outputs of every real row. Reduced variants of all five
+workloads run whole against the oracle (several tiles, ragged tails, GQA 4 and 5, with and
+without a prefix); the full-size workloads, launched exactly as the bench launches them, are
+checked on sampled rows. Invariants (padding content, batch composition, head permutation)
+must hold bit for bit."""
+
+import numpy as np
+import pytest
+
+import synth
+from helpers import ATTN_TOL, Request, run_attention, sample_rows, valid_rows
+from oracle.attention import attention_full, attention_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_full": synth.config(1),
+    "4b_like_small": synth.config(2, prefix_len=700, n_questions=6, tail_lo=30, tail_hi=140),
+    "long_document_small": synth.config(3, prefix_len=1000, n_questions=5, tail_lo=100, tail_hi=300),
+    "plain_small": synth.config(4, n_questions=40, tail_lo=1, tail_hi=70),
+    "27b_like_small": synth.config(5, prefix_len=333, n_questions=3, tail_lo=50, tail_hi=200),
+    "one_question_one_token": synth.config(1, prefix_len=1, n_questions=1, tail_lo=1, tail_hi=1),
+    "plain_single_tokens": synth.config(4, n_questions=7, tail_lo=1, tail_hi=1),
+    "prefix_one_tile": synth.config(2, prefix_len=64, n_questions=3, tail_lo=63, tail_hi=65),
+    "d64_group1": synth.config(1, n_heads_q=2, n_heads_kv=2, prefix_len=129, n_questions=9,
+                               tail_lo=1, tail_hi=40),
+    "d128_group8": synth.config(2, n_heads_q=16, n_heads_kv=2, prefix_len=90, n_questions=5,
+                                tail_lo=20, tail_hi=90),
+}
+
+
+def _oracle(req):
+    cfg, ts = req.cfg, req.tensors
+    return attention_full(ts["q"], ts["k_tail"], ts["v_tail"], ts.get("k_prefix"),
+                          ts.get("v_prefix"), req.pack["token_offset"], req.tail_len,
+                          cfg.n_heads_q, cfg.n_heads_kv, cfg.scale)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_matches_oracle_whole(name):
+    cfg = SMALL[name]
+    print(f"attention parity: {name} {cfg}", flush=True)
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    got = run_attention(req)
+    ref = _oracle(req)
+    rows = valid_rows(req)
+    assert np.isfinite(got[rows]).all()
+    err = np.abs(got[rows] - ref[rows]).max()
+    print(f"  max abs err {err:.3e} over {rows.size} rows", flush=True)
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("number", [1, 2, 3, 4, 5])
+def test_full_size_sampled(number):
+    cfg = synth.config(number)
+    print(f"attention full-size sampled parity: config {number}", flush=True)
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    got = run_attention(req)
+    samples = sample_rows(req, 160 if number != 5 else 96, seed=number)
+    ts = req.tensors
+    ref = attention_rows(ts["q"], ts["k_tail"], ts["v_tail"], ts.get("k_prefix"),
+                         ts.get("v_prefix"), req.pack["token_offset"], req.tail_len,
+                         cfg.n_heads_q, cfg.n_heads_kv, cfg.scale, samples)
+    off = req.pack["token_offset"]
+    picked = np.stack([got[off[i] + t, h] for i, t, h in samples])
+    err = np.abs(picked - ref).max()
+    print(f"  max abs err {err:.3e} over {len(samples)} sampled rows", flush=True)
+    assert np.isfinite(picked).all() and err <= ATTN_TOL
+    # every real row was written (the output starts as NaN)
+    assert np.isfinite(got[valid_rows(req)]).all()
+
+
+def test_padding_content_is_never_read():
+    cfg = SMALL["4b_like_small"]
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    a = run_attention(req)
+    rows = valid_rows(req)
+    pad = np.ones(req.pack["total_padded_tokens"], bool)
+    pad[rows] = False
+    assert pad.any()
+    ts = {k: v.copy() for k, v in req.tensors.items()}
+    big = synth.f32_to_bf16_bits(np.array([300.0], np.float32))[0]
+    for name in ("q", "k_tail", "v_tail"):
+        ts[name][pad] = big
+    b = run_attention(req, tensors=ts)
+    np.testing.assert_array_equal(a[rows], b[rows])
+
+
+def test_question_alone_is_bitwise_identical():
+    cfg = SMALL["4b_like_small"]
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    packed = run_attention(req)
+    for i in range(len(req.tail_len)):
+        off, n = req.pack["token_offset"][i], int(req.tail_len[i])
+        alone_ts = dict(req.tensors)
+        for name in ("q", "k_tail", "v_tail"):
+            alone_ts[name] = np.ascontiguousarray(req.tensors[name][off:off + n])
+        alone = run_attention(req, tensors=alone_ts, token_offset=[0], tail_len=[n])
+        np.testing.assert_array_equal(alone, packed[off:off + n])
+
+
+def test_head_permutation_within_group():
+    cfg = SMALL["27b_like_small"]
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    a = run_attention(req)
+    g = cfg.n_heads_q // cfg.n_heads_kv
+    perm = np.concatenate([np.roll(np.arange(k * g, (k + 1) * g), 2) for k in range(cfg.n_heads_kv)])
+    ts = dict(req.tensors, q=np.ascontiguousarray(req.tensors["q"][:, perm]))
+    b = run_attention(req, tensors=ts)
+    rows = valid_rows(req)
+    np.testing.assert_array_equal(a[rows][:, perm], b[rows])
+
+
+def test_out_of_range_offsets_are_skipped_not_faulted():
+    cfg = SMALL["tiny_full"]
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    good = run_attention(req)
+    offs = np.asarray(req.pack["token_offset"], np.int64).copy()
+    offs[1] = 10 ** 9  # far outside the buffer
+    got = run_attention(req, token_offset=offs)
+    for i in range(len(req.tail_len)):
+        o, n = req.pack["token_offset"][i], int(req.tail_len[i])
+        if i == 1:
+            continue
+        np.testing.assert_array_equal(got[o:o + n], good[o:o + n])

@@ -1,0 +1,90 @@
+"""GPU parity of blink_label_readout (through the C ABI) with the FP64 oracle.
+
+Bar: label probabilities within 1e-4 (max-abs), logits within 1e-4, argmax exact wherever the
+oracle's top-2 gap exceeds 1e-5 (else one of the tied maxima). All five workloads at full
+size, plus edge cases (1 and 255 options, temperature, malformed tables)."""
+
+import numpy as np
+import pytest
+
+import synth
+from helpers import LOGIT_TOL, PROB_TOL, Request, check_argmax, run_readout
+from oracle.readout import label_readout
+
+pytestmark = pytest.mark.gpu
+
+READOUT_PARTS = ("hidden", "w_u")
+
+
+def _check(req, logits, probs, arg, ids=None, off=None, last=None, temperature=None):
+    ids = req.tables.cand_ids if ids is None else ids
+    off = req.tables.cand_off if off is None else off
+    last = req.pack["last_row"] if last is None else last
+    t = req.cfg.temperature if temperature is None else temperature
+    z, p, a = label_readout(req.tensors["hidden"], last, req.tensors["w_u"], ids, off, t)
+    assert np.abs(logits - z).max() <= LOGIT_TOL
+    assert np.abs(probs - p).max() <= PROB_TOL
+    for i in range(len(last)):
+        assert abs(probs[off[i]:off[i + 1]].sum() - 1.0) <= 1e-5
+    ties = check_argmax(z, off, a, arg)
+    print(f"  logits err {np.abs(logits - z).max():.2e} probs err {np.abs(probs - p).max():.2e} "
+          f"near-ties {ties}", flush=True)
+
+
+@pytest.mark.parametrize("number", [1, 2, 3, 4, 5])
+def test_full_size(number):
+    cfg = synth.config(number)
+    print(f"readout parity: config {number}", flush=True)
+    req = Request(cfg, parts=READOUT_PARTS)
+    logits, probs, arg = run_readout(req)
+    _check(req, logits, probs, arg)
+
+
+def test_one_and_255_options():
+    cfg = synth.config(2, n_questions=3)
+    req = Request(cfg, parts=READOUT_PARTS)
+    rng = np.random.default_rng(5)
+    ids = np.concatenate([rng.choice(cfg.vocab, 1, replace=False),
+                          rng.choice(cfg.vocab, 255, replace=False),
+                          rng.choice(cfg.vocab, 7, replace=False)]).astype(np.int32)
+    off = np.array([0, 1, 256, 263], np.int32)
+    logits, probs, arg = run_readout(req, cand_ids=ids, cand_off=off)
+    assert probs[0] == 1.0 and arg[0] == 0
+    _check(req, logits, probs, arg, ids=ids, off=off)
+
+
+@pytest.mark.parametrize("temperature", [0.05, 0.7, 3.0])
+def test_temperatures(temperature):
+    req = Request(synth.config(2), parts=READOUT_PARTS)
+    logits, probs, arg = run_readout(req, temperature=temperature)
+    _check(req, logits, probs, arg, temperature=temperature)
+
+
+def test_shared_label_table():
+    # The pages' own layout: every question uses the first K_i entries of one label table.
+    cfg = synth.config(4, n_questions=64)
+    req = Request(cfg, parts=READOUT_PARTS)
+    table = np.random.default_rng(9).choice(cfg.vocab, 255, replace=False).astype(np.int32)
+    k = req.tables.n_options
+    ids = np.concatenate([table[:x] for x in k]).astype(np.int32)
+    logits, probs, arg = run_readout(req, cand_ids=ids)
+    _check(req, logits, probs, arg, ids=ids)
+
+
+def test_malformed_entries_are_flagged():
+    cfg = synth.config(1)
+    req = Request(cfg, parts=READOUT_PARTS)
+    ids = req.tables.cand_ids.copy()
+    ids[req.tables.cand_off[1]] = cfg.vocab + 5  # question 1: id out of range
+    last = np.asarray(req.pack["last_row"], np.int64).copy()
+    last[2] = -3  # question 2: row out of range
+    logits, probs, arg = run_readout(req, cand_ids=ids, last_row=last)
+    off = req.tables.cand_off
+    assert arg[1] == -1 and arg[2] == -1
+    assert np.isnan(probs[off[1]:off[2]]).all() and np.isnan(probs[off[2]:off[3]]).all()
+    good = [0, 3]
+    z, p, a = label_readout(req.tensors["hidden"], req.pack["last_row"], req.tensors["w_u"],
+                            req.tables.cand_ids, off, cfg.temperature)
+    for i in good:
+        np.testing.assert_allclose(probs[off[i]:off[i + 1]], p[off[i]:off[i + 1]], atol=PROB_TOL)
+        assert arg[i] == a[i]
