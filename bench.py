@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of this many MiB (the known-size "
+                         "reference for hardware byte counters) and exit after it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the scoring path "
@@ -92,6 +95,16 @@ def main():
 
     import synth
     import pass_typed_decision_amd as blink
+
+    if args.copy_calibration:
+        n_bytes = args.copy_calibration << 20
+        src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n_bytes}), flush=True)
+        return
 
     cfg = synth.config(args.config)
     rng = synth.rng_for(cfg)

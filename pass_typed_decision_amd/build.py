@@ -23,6 +23,9 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results in VGPRs: the attention softmax reads its score accumulators with
+    # ordinary vector instructions, and the Q fragments it pins in AGPRs feed MFMAs directly.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

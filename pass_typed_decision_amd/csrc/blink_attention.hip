@@ -11,26 +11,40 @@
 //    the rows are (real tail token, query head of the group) pairs, token-major, over all
 //    questions in question order. Padding rows are never computed, and a unit may span
 //    question boundaries, so a launch has no ragged-tile waste except at its very end.
-//  * Workgroup = 4 wave64, one per SIMD; each wave owns 64 query rows (two 32-row blocks).
-//    Every K/V tile (64 keys) is staged in LDS once and read by all four waves, i.e. one
-//    prefix tile load serves 256 query rows of up to 256/G questions' tails.
+//  * Workgroup = 8 wave64, two per SIMD; each wave owns 32 query rows. Two waves per SIMD let
+//    the hardware overlap one wave's softmax (vector ALU) with the other's matrix work. Every
+//    32x32x16 MFMA consumes 1 KiB of LDS fragment data, so the four SIMDs of a CU need
+//    128 B/clk at the full MFMA rate, below the ~200 B/clk the LDS sustains for the
+//    (bank-conflict-free) access patterns used here.
+//  * K/V tiles of 64 keys go straight from global memory into LDS (buffer loads with the LDS
+//    destination; no staging registers), in a 3-stage ring so two tiles are in flight while
+//    one is computed. The buffer descriptor's record count covers exactly the keys that are
+//    visible for the tile, so the hardware zero-fills everything past them.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: in the
-//    accumulator layout a lane holds one query and 16 keys of each 32-key block, so the row
-//    max and row sum are lane-local except for one exchange with the partner lane (l ^ 32).
-//    The probabilities then feed O^T += V^T P^T directly from registers as the B operand;
-//    V is written to LDS transposed, with the keys of each 16-key group permuted so that a
-//    lane's eight keys are contiguous and come in with one 16-byte LDS read.
-//  * Online softmax in FP32 (exp2 with scale*log2(e) folded into one FMA). The running max
-//    is only raised when a tile's max exceeds it by more than 2^8, so the O rescale (a pass
-//    over all accumulators) almost never runs; the decision is per row, so a row's result
-//    does not depend on which other rows share its wave.
+//    accumulator layout a lane holds one query and 16 keys of each 32-key block, so row max and
+//    row sum are lane-local except for one exchange with the partner lane (l ^ 32). The
+//    probabilities then feed O^T += V^T P^T from registers as the B operand; the A operand
+//    V^T comes from the row-major V tile through ds_read_b64_tr_b16 (LDS transpose reads).
+//  * LDS rows are padded (K by 16 bytes, V by 64 bytes) so that the rows one LDS cycle serves
+//    start in different banks: the K fragment reads and the V transpose reads are free of bank
+//    conflicts, and every fragment address is one base register plus an immediate offset.
+//    Each lane of a direct load computes which (row, 16-byte chunk) its fixed LDS slot holds;
+//    pad slots load out of range and receive zeros.
+//  * Softmax in FP32 on exp2. Q is pre-scaled by scale * log2(e) (rounded to bf16 once, as a
+//    standard bf16 attention does). Each row's reference m is the max of the first tile it
+//    sees; later tiles enter the S accumulator with -m as its initial value, so exp2 reads the
+//    accumulator directly, and probabilities may grow up to 2^64 above the reference (FP32
+//    and bf16 hold that with room to spare), so the O accumulators are never rescaled inside
+//    the loop. Should any row's scores exceed its reference by more than that (extreme
+//    inputs only), the workgroup recomputes exactly: one pass for the exact row maxima, then
+//    the normal pass with m fixed at them. Row sums are taken over the bf16-rounded
+//    probabilities that the PV product uses (v_dot2 with ones). Nothing a row computes depends
+//    on which other rows share its wave.
 //  * Prefix tiles first (unmasked except the last partial tile), then the tail tiles of each
 //    question the unit touches, masked per lane (same question and key <= position).
 //  * blockIdx -> (KV head, unit) puts the KV head in the low bits, so with 8 KV heads each of
 //    the 8 XCDs (dispatch is round-robin over XCDs) streams one head's prefix K/V through its
 //    own L2.
-//  * Double-buffered LDS: the next tile's global loads are issued before the current tile's
-//    MFMAs and written to the other buffer afterwards; one barrier per tile.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -40,15 +54,27 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kQB = 1;                               // 32-row query blocks per wave
+constexpr int kRowsPerWave = 32 * kQB;               // 32
+constexpr int kRowsPerUnit = kWaves * kRowsPerWave;  // 256
 constexpr int kTileKeys = 64;
+constexpr int kStages = 3;
 constexpr int kMaxGroup = 16;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLazyRescale = 8.0f;  // log2 units: probabilities stay <= 256 between rescales
+constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
+constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3 (32-bit data)
+constexpr int kWaitFlags = 0xF70;               // s_waitcnt with expcnt/lgkmcnt at their max
+constexpr bool kPinQ = true;
 
 struct Args {
   const uint16_t *q;
@@ -70,13 +96,33 @@ struct Args {
 };
 
 template <int D>
-struct Smem {
-  static constexpr int KS = D + 8;          // K row stride in bf16 (16-byte pad)
-  static constexpr int VS = kTileKeys + 8;  // V^T row stride in bf16 (16-byte pad)
-  uint16_t k[2][kTileKeys * KS];
-  uint16_t v[2][D * VS];
-  int32_t start[BLINK_MAX_QUESTIONS + 1];
+struct Layout {
+  static constexpr int KRS = D * 2 + 16;               // K row stride in LDS (bytes)
+  static constexpr int VRS = D * 2 + 64;               // V row stride in LDS (bytes)
+  static constexpr int KBYTES = kTileKeys * KRS;       // multiple of 1 KiB for D = 64, 128
+  static constexpr int VBYTES = kTileKeys * VRS;
+  static constexpr int KINST = KBYTES / 1024;          // 1 KiB direct-load instructions
+  static constexpr int VINST = VBYTES / 1024;
+  // Every wave issues the same count (the last one pads with a load into a scratch slot), so
+  // one vmcnt value is right for all of them.
+  static constexpr int PER_WAVE = (KINST + VINST + kWaves - 1) / kWaves;
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tile must be whole KiB");
 };
+
+template <int D>
+struct Smem {
+  __attribute__((aligned(16))) char k[kStages][Layout<D>::KBYTES];
+  __attribute__((aligned(16))) char v[kStages][Layout<D>::VBYTES];
+  __attribute__((aligned(16))) char pad[1024];  // target of the padding loads, never read
+  int32_t start[BLINK_MAX_QUESTIONS + 1];
+  int overflow;  // some row of the workgroup exceeded its reference by more than kHeadroom
+};
+
+// Direct-to-LDS load instructions each wave issues per tile (K and V together).
+template <int D>
+constexpr int loads_per_wave() {
+  return Layout<D>::PER_WAVE;
+}
 
 // Largest q in [0, n) with start[q] <= c (start ascending). Terminates for any contents.
 __device__ inline int find_question(const int32_t *start, int n, int64_t c) {
@@ -90,6 +136,8 @@ __device__ inline int find_question(const int32_t *start, int n, int64_t c) {
   }
   return lo;
 }
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Pair reduction over lanes l and l ^ 32 (they hold the same query, different keys).
 __device__ inline float pair_max(float x) {
@@ -105,7 +153,8 @@ __device__ inline float pair_sum(float x) {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Source of one 64-key tile: rows rowbase + kstart + [0, 64) of k/v, valid below klimit.
+
+// Source of one 64-key tile: rows rowbase + kstart + [0, 64) of k/v, visible below klimit.
 struct TileSrc {
   const uint16_t *k;
   const uint16_t *v;
@@ -117,163 +166,208 @@ struct TileSrc {
   bool valid;
 };
 
+// Global byte offset (from the tile's first row) of the 16 bytes that land in LDS byte `off`
+// of a tile with row stride RS; pad slots get an offset past every buffer (hardware zeros).
+template <int D, int RS>
+__device__ inline int slot_source(int off, int64_t stride) {
+  const int row = off / RS, chunk = (off % RS) / 16;
+  return chunk < D / 8 ? int(row * stride * 2) + chunk * 16 : 0x7ffffff0;
+}
+
+// Per-lane source offsets of this wave's direct loads (identical for every tile): load i of
+// wave w is instruction w + 4i of the tile (K instructions first, then V, then padding).
 template <int D>
-struct Stage {
-  static constexpr int KCH = kTileKeys * D / 8 / kThreads;  // 16-byte K chunks per thread
-  u32x4 k[KCH];
-  u32x4 v[4];  // 4 keys x 8 dims (threads < 2 * D)
+struct LoadPlan {
+  int voff[Layout<D>::PER_WAVE];
 };
 
 template <int D>
-__device__ inline void load_tile(const Args &a, int g, const TileSrc &s, int tid, Stage<D> &st) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
+__device__ inline LoadPlan<D> make_load_plan(const Args &a, int wave, int lane) {
+  using L = Layout<D>;
+  const int64_t stride = int64_t(a.hkv) * D;
+  LoadPlan<D> plan;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::KCH; ++i) {
-    const int ci = tid + kThreads * i;
-    const int key = ci / CPR, dch = ci % CPR;
-    const int kk = s.kstart + key;
-    const int64_t row = s.rowbase + kk;
-    st.k[i] = u32x4{0u, 0u, 0u, 0u};
-    if (kk < s.klimit && row >= 0 && row < s.rowcount)
-      st.k[i] = *reinterpret_cast<const u32x4 *>(s.k + (row * a.hkv + g) * D + dch * 8);
+  for (int i = 0; i < L::PER_WAVE; ++i) {
+    const int inst = wave + kWaves * i;
+    const int koff = inst * 1024 + lane * 16;
+    const int voff = (inst - L::KINST) * 1024 + lane * 16;
+    plan.voff[i] = inst < L::KINST ? slot_source<D, L::KRS>(koff, stride)
+                   : inst < L::KINST + L::VINST ? slot_source<D, L::VRS>(voff, stride)
+                                                : 0x7ffffff0;
   }
-  if (tid < 2 * D) {
-    const int kg = tid & 15, dc = tid >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = s.kstart + 4 * kg + r;
-      const int64_t row = s.rowbase + kk;
-      st.v[r] = u32x4{0u, 0u, 0u, 0u};
-      if (kk < s.klimit && row >= 0 && row < s.rowcount)
-        st.v[r] = *reinterpret_cast<const u32x4 *>(s.v + (row * a.hkv + g) * D + dc * 8);
-    }
-  }
+  return plan;
 }
 
+// Issues this wave's share of the direct global->LDS loads of one K/V tile.
 template <int D>
-__device__ inline void store_tile(Smem<D> &sm, int buf, int tid, const Stage<D> &st) {
-  constexpr int CPR = D / 8;
+__device__ inline void load_tile_async(const Args &a, int g, const TileSrc &s, char *lds_k,
+                                       char *lds_v, char *lds_pad, int wave,
+                                       const LoadPlan<D> &plan) {
+  using L = Layout<D>;
+  const int64_t row0 = s.rowbase + s.kstart;
+  const int64_t stride = int64_t(a.hkv) * D;  // elements between consecutive rows
+  int64_t nkeys = min(int64_t(kTileKeys), int64_t(s.klimit - s.kstart));
+  nkeys = min(nkeys, s.rowcount - row0);
+  const bool any = nkeys > 0 && row0 >= 0;
+  const int nbytes = any ? int(((nkeys - 1) * stride + D) * 2) : 0;
+  const int64_t first = any ? row0 * stride + int64_t(g) * D : 0;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(s.k + first), (short)0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(s.v + first), (short)0, nbytes, kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < Stage<D>::KCH; ++i) {
-    const int ci = tid + kThreads * i;
-    const int key = ci / CPR, dch = ci % CPR;
-    *reinterpret_cast<u32x4 *>(&sm.k[buf][key * Smem<D>::KS + dch * 8]) = st.k[i];
-  }
-  if (tid < 2 * D) {
-    const int kg = tid & 15, dc = tid >> 4;
-    // keys 4kg..4kg+3 land in slots (kg & ~3) * 4 + 4 * perm[kg & 3], perm = {0, 2, 1, 3}
-    const int sub = kg & 3;
-    const int slot = (kg >> 2) * 16 + 4 * ((sub == 1) ? 2 : (sub == 2) ? 1 : sub);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // dims 8dc + 2m (low halves) and 8dc + 2m + 1 (high halves) of the four keys
-      u32x2 even, odd;
-      even[0] = __builtin_amdgcn_perm(st.v[1][m], st.v[0][m], 0x05040100u);
-      even[1] = __builtin_amdgcn_perm(st.v[3][m], st.v[2][m], 0x05040100u);
-      odd[0] = __builtin_amdgcn_perm(st.v[1][m], st.v[0][m], 0x07060302u);
-      odd[1] = __builtin_amdgcn_perm(st.v[3][m], st.v[2][m], 0x07060302u);
-      *reinterpret_cast<u32x2 *>(&sm.v[buf][(8 * dc + 2 * m) * Smem<D>::VS + slot]) = even;
-      *reinterpret_cast<u32x2 *>(&sm.v[buf][(8 * dc + 2 * m + 1) * Smem<D>::VS + slot]) = odd;
-    }
+  for (int i = 0; i < L::PER_WAVE; ++i) {
+    const int inst = wave + kWaves * i;  // uniform
+    const bool is_k = inst < L::KINST;
+    char *dst = is_k ? lds_k + inst * 1024
+                : inst < L::KINST + L::VINST ? lds_v + (inst - L::KINST) * 1024
+                                             : lds_pad;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rk : rv, dst, 16, plan.voff[i], 0, 0, 0);
   }
 }
 
 struct RowState {
-  float m;  // running max in scaled log2 units (-inf before any visible key)
+  float m;  // running max in log2 units (-inf before any visible key)
   float l;  // this lane's partial sum of probabilities (the partner lane holds the rest)
 };
 
-// One 64-key tile for one wave, as two 32-key sub-tiles: S^T = K Q^T, online softmax,
-// O^T += V^T P^T. lim[qb]: largest visible key index within the tile minus 4 * (lane >> 5);
-// keys above it are masked (used only when MASKED).
-template <int D, int QB, bool MASKED>
-__device__ inline void compute_tile(const Smem<D> &sm, int buf, int lane, float scale_log2,
-                                    const bf16x8 (&qf)[QB][D / 16], f32x16 (&o)[QB][D / 32],
-                                    RowState (&rs)[QB], const int (&lim)[QB]) {
-  const int col = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 s[QB];  // [query block]
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
-    const uint16_t *kbase = &sm.k[buf][(kb * 32 + col) * Smem<D>::KS + 8 * half];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(kbase + ks * 16));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
-    }
+// V^T fragment for one 16-key PV step starting at key0 and 32 dims of block db:
+// lane (d = l % 32, half h) gets keys key0 + 4h + {0..3} and key0 + 8 + 4h + {0..3}.
+// `vlane` is this lane's part of the address: row 4h + r, dims 16 * (grp & 1) + 4 * cc
+// (grp = lane / 16, r = (lane % 16) / 4, cc = lane % 4).
+template <int D>
+__device__ inline int v_lane_offset(int lane) {
+  const int grp = lane >> 4, i = lane & 15, r = i >> 2, cc = i & 3, h = lane >> 5;
+  return (4 * h + r) * Layout<D>::VRS + (16 * (grp & 1) + 4 * cc) * 2;
+}
+template <int D>
+__device__ inline bf16x8 read_v(const char *vt, int vlane, int key0, int db) {
+  lds_char *base = (lds_char *)vt + vlane + key0 * Layout<D>::VRS + db * 64;
+  const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)base);
+  const bf16x4 t1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + 8 * Layout<D>::VRS));
+  return bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+}
 
-    float factor[QB];
-    bool rescale = false;
+// Probabilities of one 16-value accumulator slice into bf16 B operands, with row-sum update.
+__device__ inline void probs_to_bf16(const f32x16 &s, float delta, bf16x8 (&pb)[2], float &l) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(s[8 * c + e] - delta),
+                         (__bf16)__builtin_amdgcn_exp2f(s[8 * c + e + 1] - delta)};
+      pb[c][e] = p2[0];
+      pb[c][e + 1] = p2[1];
+      l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
+    }
+  }
+}
+
+// One 32-key sub-tile for one wave: S'^T = K Q'^T - m, online softmax, O^T += V^T P^T.
+// lim[qb]: largest visible key index within the sub-tile minus 4 * (lane >> 5); keys above it
+// are masked (used only when MASKED).
+// O^T += V^T P^T over one 32-key sub-tile (two 16-key MFMA steps per 32-dim block).
+template <int D>
+__device__ inline void pv_product(const char *vt, int key0, const bf16x8 (&pb)[kQB][2],
+                                  f32x16 (&o)[kQB][D / 32]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16x8 vf = read_v<D>(vt, 0, key0 + 16 * c, db);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb][c], o[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+// kt/vt point at the tile plus this lane's part of the fragment addresses.
+// MAX_ONLY: only the row maxima are taken (raw scores, log2 units) for the exact pass.
+// Returns true when some row of this wave exceeded its reference by more than kHeadroom.
+template <int D, bool MAX_ONLY>
+__device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
+                                       bf16x8 (&qf)[kQB][D / 16],
+                                       f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB],
+                                       bool masked, const int (&lim)[kQB]) {
+  f32x16 s[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float init = (MAX_ONLY || rs[qb].m == -INFINITY) ? 0.0f : -rs[qb].m;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[qb][v] = init;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 kf = as_bf16x8(
+        *reinterpret_cast<const u32x4 *>(kt + key0 * Layout<D>::KRS + ks * 32));
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      // The Q fragments are only ever MFMA B operands, which can be read from AGPRs: keep them
+      // there and leave the VGPRs to the scores and accumulators (emits no instruction).
+      if (kPinQ) asm volatile("" : "+a"(qf[qb][ks]));
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
+    }
+  }
+
+  if (masked) {  // uniform: tail tiles and the last partial prefix tile
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = s[qb][v];
-        if (MASKED) {
-          const int key = kb * 32 + 8 * (v >> 2) + (v & 3);
-          x = (key <= lim[qb]) ? x : -INFINITY;
-          s[qb][v] = x;
-        }
-        mx = fmaxf(mx, x);
-      }
-      const float mt = pair_max(mx) * scale_log2;
-      const float m_old = rs[qb].m;
-      const float m_new = (mt > m_old + kLazyRescale) ? mt : m_old;
-      factor[qb] = (m_new == m_old) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
-      rescale |= factor[qb] != 1.0f;
-      rs[qb].m = m_new;
-      const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-      float sum = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][v], scale_log2, -base));
-        s[qb][v] = p;
-        sum += p;
-      }
-      rs[qb].l = rs[qb].l * factor[qb] + sum;
-    }
-    if (__builtin_amdgcn_ballot_w64(rescale)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[qb][db] *= factor[qb];
-    }
-
-    const uint16_t *vbase = &sm.v[buf][col * Smem<D>::VS + 8 * half + 32 * kb];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pb[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[qb][e] = (__bf16)s[qb][8 * c + e];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 vf =
-            as_bf16x8(*reinterpret_cast<const u32x4 *>(vbase + db * 32 * Smem<D>::VS + 16 * c));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb], o[qb][db], 0, 0, 0);
+        const int key = 8 * (v >> 2) + (v & 3);
+        s[qb][v] = (key <= lim[qb]) ? s[qb][v] : -INFINITY;
       }
     }
   }
+  float mx[kQB];
+  bool fresh_any = false, over = false;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float m = s[qb][0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) m = fmaxf(m, s[qb][v]);
+    mx[qb] = pair_max(m);
+    if (MAX_ONLY) {
+      rs[qb].m = fmaxf(rs[qb].m, mx[qb]);
+    } else if (rs[qb].m == -INFINITY) {
+      fresh_any |= mx[qb] > -INFINITY;
+    } else {
+      over |= mx[qb] > kHeadroom;
+    }
+  }
+  if (MAX_ONLY) return false;
+
+  bf16x8 pb[kQB][2];
+  if (__builtin_amdgcn_ballot_w64(fresh_any)) {
+    // First visible keys of some row: its reference becomes this tile's max (its O and l
+    // are still zero). Other rows subtract 0, bit-identical to the common path.
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const bool fresh = rs[qb].m == -INFINITY && mx[qb] > -INFINITY;
+      const float delta = fresh ? mx[qb] : 0.0f;
+      if (fresh) rs[qb].m = mx[qb];
+      probs_to_bf16(s[qb], delta, pb[qb], rs[qb].l);
+    }
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[qb], 0.0f, pb[qb], rs[qb].l);
+  }
+  pv_product<D>(vt, key0, pb, o);
+  return over;
 }
 
 struct Unit {
   int qa, qz, posz;  // questions touched by the workgroup; last row's position in qz
 };
 
-__device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const Unit &u, int q,
-                                    int g) {
-  (void)g;
+__device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const Unit &u, int q) {
   TileSrc s{};
   s.valid = false;
   for (; q <= u.qz; ++q) {
-    const int nq = start[q + 1] - start[q];
+    const int nq = uniform(start[q + 1] - start[q]);
     const int limit = (q == u.qz) ? u.posz + 1 : nq;
     // A malformed table cannot make the loop run past the context length.
     if (limit > 0 && limit <= nq && nq <= BLINK_MAX_INPUT_TOKENS) {
@@ -291,7 +385,7 @@ __device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const U
   return s;
 }
 
-__device__ inline TileSrc first_tile(const Args &a, const int32_t *start, const Unit &u, int g) {
+__device__ inline TileSrc first_tile(const Args &a, const int32_t *start, const Unit &u) {
   if (a.prefix_len > 0) {
     TileSrc s{};
     s.k = a.k_pre;
@@ -304,137 +398,123 @@ __device__ inline TileSrc first_tile(const Args &a, const int32_t *start, const 
     s.valid = true;
     return s;
   }
-  return tail_from(a, start, u, u.qa, g);
+  return tail_from(a, start, u, u.qa);
 }
 
 __device__ inline TileSrc next_tile(const Args &a, const int32_t *start, const Unit &u,
-                                    TileSrc s, int g) {
+                                    TileSrc s) {
+  if (!s.valid) return s;
   s.kstart += kTileKeys;
   if (s.kstart < s.klimit) return s;
-  return tail_from(a, start, u, s.q < 0 ? u.qa : s.q + 1, g);
+  return tail_from(a, start, u, s.q < 0 ? u.qa : s.q + 1);
 }
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args a) {
-  constexpr int kRowsPerWave = 32 * QB;
-  constexpr int kRowsPerUnit = 4 * kRowsPerWave;
-  __shared__ __attribute__((aligned(16))) Smem<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, half = lane >> 5;
-  const int G = a.group;
-  const int g = int(blockIdx.x % unsigned(a.hkv));
-  const int64_t unit = blockIdx.x / unsigned(a.hkv);
+struct RowTables {
+  const int (&rq)[kQB];    // question of each of this lane's rows (-1 if not a real row)
+  const int (&rpos)[kQB];  // tail position of each row
+};
+struct WaveSpan {
+  bool active;     // the wave has at least one real row
+  int qa, qz, posz;  // questions the wave's rows touch; last row's position in qz
+};
 
-  for (int i = tid; i <= a.n; i += kThreads) sm.start[i] = a.valid_start[i];
-  __syncthreads();
-  const int64_t valid_total = min(int64_t(sm.start[a.n]), a.total_valid);
-  const int64_t R = valid_total * G;
-  const int64_t row0 = unit * kRowsPerUnit;
-  if (row0 >= R) return;  // uniform across the workgroup
-
-  // This lane's two query rows.
-  bool rvalid[QB];
-  int rq[QB], rpos[QB], rhead[QB];
-  int64_t rtok[QB];
-  bf16x8 qf[QB][D / 16];
+template <int D>
+__device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], bool reset_m) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int64_t r = row0 + wave * kRowsPerWave + qb * 32 + col;
-    rvalid[qb] = r < R;
-    const int64_t c = rvalid[qb] ? r / G : 0;
-    const int hl = int(r % G);
-    const int q = find_question(sm.start, a.n, c);
-    const int nq = sm.start[q + 1] - sm.start[q];
-    const int pos = int(c - sm.start[q]);
-    rvalid[qb] = rvalid[qb] && pos >= 0 && pos < nq;
-    const int64_t tok = a.token_offset[q] + pos;
-    rvalid[qb] = rvalid[qb] && tok >= 0 && tok < a.t_pad;
-    rq[qb] = rvalid[qb] ? q : -1;
-    rpos[qb] = pos;
-    rtok[qb] = tok;
-    rhead[qb] = g * G + hl;
-    const uint16_t *qrow = a.q + ((rvalid[qb] ? tok : 0) * a.hq + rhead[qb]) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (rvalid[qb]) v = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
-      qf[qb][ks] = as_bf16x8(v);
-    }
-  }
-
-  // Questions touched by the workgroup and by this wave.
-  Unit u;
-  {
-    const int64_t c0 = row0 / G, cz = (min(row0 + kRowsPerUnit, R) - 1) / G;
-    u.qa = find_question(sm.start, a.n, c0);
-    u.qz = find_question(sm.start, a.n, cz);
-    u.posz = int(cz - sm.start[u.qz]);
-  }
-  const int64_t wr0 = row0 + wave * kRowsPerWave;
-  const bool wave_active = wr0 < R;
-  int wqa = 0, wqz = -1, wposz = -1;
-  if (wave_active) {
-    const int64_t c0 = wr0 / G, cz = (min(wr0 + kRowsPerWave, R) - 1) / G;
-    wqa = find_question(sm.start, a.n, c0);
-    wqz = find_question(sm.start, a.n, cz);
-    wposz = int(cz - sm.start[wqz]);
-  }
-
-  f32x16 o[QB][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[qb][db] = f32x16{};
-  RowState rs[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) rs[qb] = RowState{-INFINITY, 0.f};
+    rs[qb].l = 0.f;
+    if (reset_m) rs[qb].m = -INFINITY;
+  }
+}
 
-  TileSrc cur = first_tile(a, sm.start, u, g);
-  if (!cur.valid) return;  // uniform: nothing visible (cannot happen for a valid table)
-  Stage<D> st;
-  load_tile<D>(a, g, cur, tid, st);
-  store_tile<D>(sm, 0, tid, st);
+// All tiles of the unit through the 3-stage LDS ring; max_only collects exact row maxima.
+// Returns true when a row of this wave exceeded its reference by more than kHeadroom.
+template <int D>
+__device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
+                                 const TileSrc &first, const RowTables &rt, const WaveSpan &ws,
+                                 int klane, int vlane, int wave, int lane,
+                                 bf16x8 (&qf)[kQB][D / 16], f32x16 (&o)[kQB][D / 32],
+                                 RowState (&rs)[kQB], bool max_only) {
+  const int half = lane >> 5;
+  const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
+  bool over = false;
+  // Tile t lives in stage t % 3; loads for tile t + 2 are issued before tile t is computed.
+  // The only vector memory operations inside the loop are these tile loads, so waiting for
+  // all but the newest tile's loads (vmcnt) means the previous tile has landed.
+  TileSrc cur = first;
+  TileSrc nxt = next_tile(a, sm.start, u, cur);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile_async<D>(a, g, cur, sm.k[0], sm.v[0], sm.pad, wave, plan);
+  if (nxt.valid) load_tile_async<D>(a, g, nxt, sm.k[1], sm.v[1], sm.pad, wave, plan);
+  __builtin_amdgcn_sched_barrier(0);
+  if (nxt.valid)
+    __builtin_amdgcn_s_waitcnt(kWaitFlags | loads_per_wave<D>());
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitFlags);
   __syncthreads();
-  int buf = 0;
+  int stage = 0;
   while (true) {
-    const TileSrc nxt = next_tile(a, sm.start, u, cur, g);
-    if (nxt.valid) load_tile<D>(a, g, nxt, tid, st);
+    const TileSrc after = next_tile(a, sm.start, u, nxt);
+    const int stage2 = stage >= 1 ? stage - 1 : 2;  // (stage + 2) % 3
+    __builtin_amdgcn_sched_barrier(0);
+    if (after.valid)
+      load_tile_async<D>(a, g, after, sm.k[stage2], sm.v[stage2], sm.pad, wave, plan);
+    __builtin_amdgcn_sched_barrier(0);
 
-    bool active = wave_active;
+    bool active = ws.active;
     if (cur.q >= 0)
-      active = active && cur.q >= wqa && cur.q <= wqz && !(cur.q == wqz && cur.kstart > wposz);
+      active = active && cur.q >= ws.qa && cur.q <= ws.qz &&
+               !(cur.q == ws.qz && cur.kstart > ws.posz);
     if (active) {
-      if (cur.q < 0 && cur.kstart + kTileKeys <= a.prefix_len) {
-        int lim[QB];
+      const char *kt = sm.k[stage] + klane;
+      const char *vt = sm.v[stage] + vlane;
+#pragma unroll 1
+      for (int sub = 0; sub < 2; ++sub) {
+        const int base = cur.kstart + 32 * sub;  // first key of the sub-tile
+        const bool masked = !(cur.q < 0 && base + 32 <= a.prefix_len);
+        int lim[kQB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) lim[qb] = kTileKeys;
-        compute_tile<D, QB, false>(sm, buf, lane, a.scale_log2, qf, o, rs, lim);
-      } else {
-        int lim[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          int last;  // last visible key of this row, relative to the tile start
+        for (int qb = 0; qb < kQB; ++qb) {
+          int last;  // last visible key of this row, relative to the sub-tile start
           if (cur.q < 0)
-            last = a.prefix_len - 1 - cur.kstart;
+            last = a.prefix_len - 1 - base;
           else
-            last = (rq[qb] == cur.q) ? rpos[qb] - cur.kstart : -1;
-          last = min(last, kTileKeys - 1);
+            last = (rt.rq[qb] == cur.q) ? rt.rpos[qb] - base : -1;
+          last = min(last, 31);
           lim[qb] = last - 4 * half;
         }
-        compute_tile<D, QB, true>(sm, buf, lane, a.scale_log2, qf, o, rs, lim);
+        if (max_only)
+          compute_subtile<D, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+        else
+          over |= compute_subtile<D, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
       }
     }
 
-    if (nxt.valid) store_tile<D>(sm, buf ^ 1, tid, st);
+    // This wave's loads of tile t + 1 have landed once only tile t + 2's remain in flight;
+    // the barrier then covers every wave's part.
+    __builtin_amdgcn_sched_barrier(0);
+    if (after.valid)
+      __builtin_amdgcn_s_waitcnt(kWaitFlags | loads_per_wave<D>());
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitFlags);
     __syncthreads();
     if (!nxt.valid) break;
     cur = nxt;
-    buf ^= 1;
+    nxt = after;
+    stage = stage == 2 ? 0 : stage + 1;
   }
+  return over;
+}
 
-  // Normalise and store bf16 rows (four consecutive dims per 8-byte store).
+// Normalise and store bf16 rows (four consecutive dims per 8-byte store).
+template <int D>
+__device__ inline void store_rows(const Args &a, const f32x16 (&o)[kQB][D / 32],
+                                  const RowState (&rs)[kQB], const bool (&rvalid)[kQB],
+                                  const int64_t (&rtok)[kQB], const int (&rhead)[kQB], int half) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+  for (int qb = 0; qb < kQB; ++qb) {
     const float l = pair_sum(rs[qb].l);
     if (!rvalid[qb]) continue;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -457,14 +537,112 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   }
 }
 
-template <int D, int QB>
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args a) {
+  __shared__ Smem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = a.group;
+  const int g = int(blockIdx.x % unsigned(a.hkv));
+  const int64_t unit = blockIdx.x / unsigned(a.hkv);
+
+  for (int i = tid; i <= a.n; i += kThreads) sm.start[i] = a.valid_start[i];
+  if (tid == 0) sm.overflow = 0;
+  __syncthreads();
+  const int64_t valid_total = min(int64_t(uniform(sm.start[a.n])), a.total_valid);
+  const int64_t R = valid_total * G;
+  const int64_t row0 = unit * kRowsPerUnit;
+  if (row0 >= R) return;  // uniform across the workgroup
+
+  // Questions touched by the workgroup and by this wave.
+  Unit u;
+  {
+    const int64_t c0 = row0 / G, cz = (min(row0 + kRowsPerUnit, R) - 1) / G;
+    u.qa = uniform(find_question(sm.start, a.n, c0));
+    u.qz = uniform(find_question(sm.start, a.n, cz));
+    u.posz = uniform(int(cz - sm.start[u.qz]));
+  }
+  const int64_t wr0 = row0 + wave * kRowsPerWave;
+  const bool wave_active = wr0 < R;
+  int wqa = 0, wqz = -1, wposz = -1;
+  if (wave_active) {
+    const int64_t c0 = wr0 / G, cz = (min(wr0 + kRowsPerWave, R) - 1) / G;
+    wqa = uniform(find_question(sm.start, a.n, c0));
+    wqz = uniform(find_question(sm.start, a.n, cz));
+    wposz = uniform(int(cz - sm.start[wqz]));
+  }
+
+  // This lane's query rows: Q pre-scaled by scale * log2(e), rounded to bf16 once.
+  bool rvalid[kQB];
+  int rq[kQB], rpos[kQB], rhead[kQB];
+  int64_t rtok[kQB];
+  bf16x8 qf[kQB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int64_t r = row0 + wave * kRowsPerWave + qb * 32 + col;
+    rvalid[qb] = r < R;
+    const int64_t c = rvalid[qb] ? r / G : 0;
+    const int hl = int(r % G);
+    const int q = find_question(sm.start, a.n, c);
+    const int nq = sm.start[q + 1] - sm.start[q];
+    const int pos = int(c - sm.start[q]);
+    rvalid[qb] = rvalid[qb] && pos >= 0 && pos < nq;
+    const int64_t tok = a.token_offset[q] + pos;
+    rvalid[qb] = rvalid[qb] && tok >= 0 && tok < a.t_pad;
+    rq[qb] = rvalid[qb] ? q : -1;
+    rpos[qb] = pos;
+    rtok[qb] = tok;
+    rhead[qb] = g * G + hl;
+    const uint16_t *qrow = a.q + ((rvalid[qb] ? tok : 0) * a.hq + rhead[qb]) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rvalid[qb]) v = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
+      const bf16x8 x = as_bf16x8(v);
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * a.scale_log2);
+      qf[qb][ks] = y;
+    }
+  }
+
+  // Lane parts of the fragment addresses: K rows col (+ key0), chunk half (+ 2 ks).
+  const int klane = col * Layout<D>::KRS + 16 * half;
+  const int vlane = v_lane_offset<D>(lane);
+
+  const TileSrc first = first_tile(a, sm.start, u);
+  if (!first.valid) return;  // uniform: nothing visible (cannot happen for a valid table)
+
+  const RowTables rt{rq, rpos};
+  const WaveSpan ws{wave_active, wqa, wqz, wposz};
+  f32x16 o[kQB][D / 32];
+  RowState rs[kQB];
+  init_rows<D>(o, rs, true);
+  const bool over =
+      run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
+  store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
+  // Did any wave of the workgroup overflow? (The flag was cleared before the first barrier.)
+  if (__builtin_amdgcn_ballot_w64(over)) sm.overflow = 1;
+  __syncthreads();
+  if (sm.overflow) {
+    // Extreme inputs only: exact row maxima first, then the normal pass with those references;
+    // its rows overwrite the ones just stored. (The accumulators are reused: the stored values
+    // are dead, so nothing has to be merged.)
+    init_rows<D>(o, rs, true);
+    run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, true);
+    init_rows<D>(o, rs, false);
+    run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
+    store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
+  }
+}
+
+template <int D>
 hipError_t launch(const Args &a, hipStream_t stream) {
-  constexpr int kRowsPerUnit = 4 * 32 * QB;
   const int64_t rows = a.total_valid * a.group;
   const int64_t units = (rows + kRowsPerUnit - 1) / kRowsPerUnit;
   const int64_t blocks = units * a.hkv;
-  hipLaunchKernelGGL((prefix_tail_attention_kernel<D, QB>), dim3(unsigned(blocks)), dim3(kThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL(prefix_tail_attention_kernel<D>, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -494,6 +672,10 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
       n_heads_q / n_heads_kv > kMaxGroup)
     return fail(BLINK_E_INVALID, "head counts %d/%d: need H_q a multiple of H_kv, group <= %d",
                 n_heads_q, n_heads_kv, kMaxGroup);
+  // A 64-key tile's byte span from its first row must fit a 32-bit buffer offset.
+  if (int64_t(kTileKeys) * n_heads_kv * head_dim * 2 >= (int64_t(1) << 31))
+    return fail(BLINK_E_LIMIT, "%d KV heads of %d dims are too wide for one tile", n_heads_kv,
+                head_dim);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(BLINK_E_INVALID, "scale must be finite and positive");
   if (total_valid_tokens < n_questions || total_padded_tokens < total_valid_tokens ||
@@ -502,9 +684,11 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
                 "questions", (long long)total_valid_tokens, (long long)total_padded_tokens,
                 n_questions);
   const int64_t blocks =
-      (total_valid_tokens * (n_heads_q / n_heads_kv) + 127) / 128 * n_heads_kv;
+      (total_valid_tokens * (n_heads_q / n_heads_kv) + kRowsPerUnit - 1) / kRowsPerUnit *
+      n_heads_kv;
   if (blocks > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "launch too large");
-  const void *ptrs[] = {q, k_tail, v_tail, out, prefix_len ? k_prefix : q, prefix_len ? v_prefix : q};
+  const void *ptrs[] = {q, k_tail, v_tail, out, prefix_len ? k_prefix : q,
+                        prefix_len ? v_prefix : q};
   for (const void *p : ptrs)
     if (!blink::aligned16(p)) return fail(BLINK_E_INVALID, "tensors must be 16-byte aligned");
 
@@ -527,8 +711,8 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
   a.scale_log2 = scale * kLog2e;
 
   (void)hipGetLastError();
-  const hipError_t err = head_dim == 64 ? launch<64, 2>(a, static_cast<hipStream_t>(stream))
-                                        : launch<128, 1>(a, static_cast<hipStream_t>(stream));
+  const hipError_t err = head_dim == 64 ? launch<64>(a, static_cast<hipStream_t>(stream))
+                                        : launch<128>(a, static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
     return fail(BLINK_E_DEVICE, "blink_prefix_tail_attention launch: %s", hipGetErrorString(err));
   return blink::ok();
