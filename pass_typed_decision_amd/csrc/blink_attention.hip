@@ -74,7 +74,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3 (32-bit data)
 constexpr int kWaitFlags = 0xF70;               // s_waitcnt with expcnt/lgkmcnt at their max
-constexpr bool kPinQ = true;
 
 struct Args {
   const uint16_t *q;
@@ -103,9 +102,12 @@ struct Layout {
   static constexpr int VBYTES = kTileKeys * VRS;
   static constexpr int KINST = KBYTES / 1024;          // 1 KiB direct-load instructions
   static constexpr int VINST = VBYTES / 1024;
-  // Every wave issues the same count (the last one pads with a load into a scratch slot), so
-  // one vmcnt value is right for all of them.
-  static constexpr int PER_WAVE = (KINST + VINST + kWaves - 1) / kWaves;
+  // Instruction i of a tile is issued by wave i % kWaves: every wave issues FULL loads, the
+  // first EXTRA waves one more.
+  static constexpr int TOTAL = KINST + VINST;
+  static constexpr int FULL = TOTAL / kWaves;
+  static constexpr int EXTRA = TOTAL % kWaves;
+  static constexpr int PER_WAVE = FULL + (EXTRA > 0);
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tile must be whole KiB");
 };
 
@@ -113,15 +115,20 @@ template <int D>
 struct Smem {
   __attribute__((aligned(16))) char k[kStages][Layout<D>::KBYTES];
   __attribute__((aligned(16))) char v[kStages][Layout<D>::VBYTES];
-  __attribute__((aligned(16))) char pad[1024];  // target of the padding loads, never read
   int32_t start[BLINK_MAX_QUESTIONS + 1];
   int overflow;  // some row of the workgroup exceeded its reference by more than kHeadroom
 };
 
-// Direct-to-LDS load instructions each wave issues per tile (K and V together).
+// Waits until at most one tile's loads of this wave are in flight (the newest tile's), or none.
 template <int D>
-constexpr int loads_per_wave() {
-  return Layout<D>::PER_WAVE;
+__device__ inline void wait_tile_loads(int wave, bool keep_one) {
+  using L = Layout<D>;
+  if (!keep_one)
+    __builtin_amdgcn_s_waitcnt(kWaitFlags);
+  else if (L::EXTRA > 0 && wave < L::EXTRA)
+    __builtin_amdgcn_s_waitcnt(kWaitFlags | (L::FULL + 1));
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitFlags | L::FULL);
 }
 
 // Largest q in [0, n) with start[q] <= c (start ascending). Terminates for any contents.
@@ -175,7 +182,7 @@ __device__ inline int slot_source(int off, int64_t stride) {
 }
 
 // Per-lane source offsets of this wave's direct loads (identical for every tile): load i of
-// wave w is instruction w + 4i of the tile (K instructions first, then V, then padding).
+// wave w is instruction w + kWaves * i of the tile (K instructions first, then V).
 template <int D>
 struct LoadPlan {
   int voff[Layout<D>::PER_WAVE];
@@ -192,38 +199,53 @@ __device__ inline LoadPlan<D> make_load_plan(const Args &a, int wave, int lane) 
     const int koff = inst * 1024 + lane * 16;
     const int voff = (inst - L::KINST) * 1024 + lane * 16;
     plan.voff[i] = inst < L::KINST ? slot_source<D, L::KRS>(koff, stride)
-                   : inst < L::KINST + L::VINST ? slot_source<D, L::VRS>(voff, stride)
-                                                : 0x7ffffff0;
+                                   : slot_source<D, L::VRS>(voff, stride);
   }
   return plan;
 }
 
-// Issues this wave's share of the direct global->LDS loads of one K/V tile.
+// Buffer descriptors of one tile's K and V rows; their record counts end at the last visible
+// key (and at the tensor's end), so every load past them reads zeros. An invalid tile gets
+// empty descriptors: its loads write zeros into a free stage.
+struct TileRsrc {
+  __amdgpu_buffer_rsrc_t k, v;
+};
+
 template <int D>
-__device__ inline void load_tile_async(const Args &a, int g, const TileSrc &s, char *lds_k,
-                                       char *lds_v, char *lds_pad, int wave,
-                                       const LoadPlan<D> &plan) {
-  using L = Layout<D>;
+__device__ inline TileRsrc tile_rsrc(const Args &a, int g, const TileSrc &s) {
   const int64_t row0 = s.rowbase + s.kstart;
   const int64_t stride = int64_t(a.hkv) * D;  // elements between consecutive rows
   int64_t nkeys = min(int64_t(kTileKeys), int64_t(s.klimit - s.kstart));
   nkeys = min(nkeys, s.rowcount - row0);
-  const bool any = nkeys > 0 && row0 >= 0;
+  const bool any = s.valid && nkeys > 0 && row0 >= 0;
   const int nbytes = any ? int(((nkeys - 1) * stride + D) * 2) : 0;
   const int64_t first = any ? row0 * stride + int64_t(g) * D : 0;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(s.k + first), (short)0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(s.v + first), (short)0, nbytes, kBufferFlags);
+  const uint16_t *kb = s.valid ? s.k : nullptr, *vb = s.valid ? s.v : nullptr;
+  return TileRsrc{
+      __builtin_amdgcn_make_buffer_rsrc((void *)(kb + first), (short)0, nbytes, kBufferFlags),
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vb + first), (short)0, nbytes, kBufferFlags)};
+}
+
+// Issues load i (a plan entry; the caller keeps i < FULL, or i == FULL only for the first
+// EXTRA waves) of one tile into the given stage.
+template <int D>
+__device__ inline void issue_load(const TileRsrc &r, char *lds_k, char *lds_v, int wave,
+                                  const LoadPlan<D> &plan, int i) {
+  using L = Layout<D>;
+  const int inst = wave + kWaves * i;  // uniform
+  const bool is_k = inst < L::KINST;
+  char *dst = is_k ? lds_k + inst * 1024 : lds_v + (inst - L::KINST) * 1024;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? r.k : r.v, dst, 16, plan.voff[i], 0, 0, 0);
+}
+
+// All of this wave's loads of one tile.
+template <int D>
+__device__ inline void load_tile_async(const TileRsrc &r, char *lds_k, char *lds_v, int wave,
+                                       const LoadPlan<D> &plan) {
+  using L = Layout<D>;
 #pragma unroll
-  for (int i = 0; i < L::PER_WAVE; ++i) {
-    const int inst = wave + kWaves * i;  // uniform
-    const bool is_k = inst < L::KINST;
-    char *dst = is_k ? lds_k + inst * 1024
-                : inst < L::KINST + L::VINST ? lds_v + (inst - L::KINST) * 1024
-                                             : lds_pad;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rk : rv, dst, 16, plan.voff[i], 0, 0, 0);
-  }
+  for (int i = 0; i < L::FULL; ++i) issue_load<D>(r, lds_k, lds_v, wave, plan, i);
+  if (L::EXTRA > 0 && wave < L::EXTRA) issue_load<D>(r, lds_k, lds_v, wave, plan, L::FULL);
 }
 
 struct RowState {
@@ -304,12 +326,8 @@ __device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
     const bf16x8 kf = as_bf16x8(
         *reinterpret_cast<const u32x4 *>(kt + key0 * Layout<D>::KRS + ks * 32));
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      // The Q fragments are only ever MFMA B operands, which can be read from AGPRs: keep them
-      // there and leave the VGPRs to the scores and accumulators (emits no instruction).
-      if (kPinQ) asm volatile("" : "+a"(qf[qb][ks]));
+    for (int qb = 0; qb < kQB; ++qb)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
-    }
   }
 
   if (masked) {  // uniform: tail tiles and the last partial prefix tile
@@ -356,6 +374,68 @@ __device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
     for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[qb], 0.0f, pb[qb], rs[qb].l);
   }
   pv_product<D>(vt, key0, pb, o);
+  return over;
+}
+
+// A full, unmasked 64-key tile for a wave whose rows all have their reference already (the
+// common case: every prefix tile after the first). Both 32-key score blocks are computed
+// first, all in one basic block, so one block's softmax (vector ALU) can be interleaved with
+// the other block's matrix products. Returns true when a row exceeded its headroom.
+// The next tile's FULL regular loads are issued between the score MFMAs, one per 4 MFMAs, so
+// the waves of a CU do not all queue their loads at once after the barrier.
+template <int D>
+__device__ inline bool compute_tile_fast(const char *kt, const char *vt,
+                                         bf16x8 (&qf)[kQB][D / 16], f32x16 (&o)[kQB][D / 32],
+                                         RowState (&rs)[kQB], const TileRsrc &load_src,
+                                         char *next_k, char *next_v, int wave,
+                                         const LoadPlan<D> &plan) {
+  constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+  constexpr int kSteps = 2 * (D / 16);  // score MFMA steps (each kQB MFMAs) in the tile
+  f32x16 s[2][kQB];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float init = -rs[qb].m;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[sub][qb][v] = init;
+    }
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 kf = as_bf16x8(
+          *reinterpret_cast<const u32x4 *>(kt + 32 * sub * Layout<D>::KRS + ks * 32));
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        s[sub][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[sub][qb], 0, 0, 0);
+      const int step = sub * (D / 16) + ks;
+      if (step % 4 == 3 && step / 4 < Layout<D>::FULL)
+        issue_load<D>(load_src, next_k, next_v, wave, plan, step / 4);
+    }
+  }
+  // Keep that order: K fragment read, its MFMAs, and a tile load after every fourth step.
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kQB, 0);
+    if (step % 4 == 3 && step / 4 < Layout<D>::FULL)
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+  }
+  bool over = false;
+  bf16x8 pb[2][kQB][2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float m = s[sub][qb][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[sub][qb][v]);
+      over |= pair_max(m) > kHeadroom;
+      probs_to_bf16(s[sub][qb], 0.0f, pb[sub][qb], rs[qb].l);
+    }
+    pv_product<D>(vt, 32 * sub, pb[sub], o);
+  }
   return over;
 }
 
@@ -446,28 +526,40 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   TileSrc cur = first;
   TileSrc nxt = next_tile(a, sm.start, u, cur);
   __builtin_amdgcn_sched_barrier(0);
-  load_tile_async<D>(a, g, cur, sm.k[0], sm.v[0], sm.pad, wave, plan);
-  if (nxt.valid) load_tile_async<D>(a, g, nxt, sm.k[1], sm.v[1], sm.pad, wave, plan);
+  load_tile_async<D>(tile_rsrc<D>(a, g, cur), sm.k[0], sm.v[0], wave, plan);
+  load_tile_async<D>(tile_rsrc<D>(a, g, nxt), sm.k[1], sm.v[1], wave, plan);
   __builtin_amdgcn_sched_barrier(0);
-  if (nxt.valid)
-    __builtin_amdgcn_s_waitcnt(kWaitFlags | loads_per_wave<D>());
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitFlags);
+  wait_tile_loads<D>(wave, true);
   __syncthreads();
   int stage = 0;
   while (true) {
+    // Tile t + 2 (zeros if it does not exist) goes into the stage tile t - 1 used.
     const TileSrc after = next_tile(a, sm.start, u, nxt);
     const int stage2 = stage >= 1 ? stage - 1 : 2;  // (stage + 2) % 3
+    const TileRsrc ra = tile_rsrc<D>(a, g, after);
     __builtin_amdgcn_sched_barrier(0);
-    if (after.valid)
-      load_tile_async<D>(a, g, after, sm.k[stage2], sm.v[stage2], sm.pad, wave, plan);
-    __builtin_amdgcn_sched_barrier(0);
+    if (Layout<D>::EXTRA > 0 && wave < Layout<D>::EXTRA)
+      issue_load<D>(ra, sm.k[stage2], sm.v[stage2], wave, plan, Layout<D>::FULL);
 
     bool active = ws.active;
     if (cur.q >= 0)
       active = active && cur.q >= ws.qa && cur.q <= ws.qz &&
                !(cur.q == ws.qz && cur.kstart > ws.posz);
-    if (active) {
+    bool fresh = false;  // some row of this wave has not seen a visible key yet
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) fresh |= rs[qb].m == -INFINITY;
+    const bool fast = !max_only && cur.q < 0 && cur.kstart + kTileKeys <= a.prefix_len &&
+                      !__builtin_amdgcn_ballot_w64(fresh);
+    if (active && fast) {
+      over |= compute_tile_fast<D>(sm.k[stage] + klane, sm.v[stage] + vlane, qf, o, rs, ra,
+                                   sm.k[stage2], sm.v[stage2], wave, plan);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Layout<D>::FULL; ++i)
+        issue_load<D>(ra, sm.k[stage2], sm.v[stage2], wave, plan, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (active && !fast) {
       const char *kt = sm.k[stage] + klane;
       const char *vt = sm.v[stage] + vlane;
 #pragma unroll 1
@@ -495,16 +587,17 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     // This wave's loads of tile t + 1 have landed once only tile t + 2's remain in flight;
     // the barrier then covers every wave's part.
     __builtin_amdgcn_sched_barrier(0);
-    if (after.valid)
-      __builtin_amdgcn_s_waitcnt(kWaitFlags | loads_per_wave<D>());
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitFlags);
+    wait_tile_loads<D>(wave, true);
     __syncthreads();
     if (!nxt.valid) break;
     cur = nxt;
     nxt = after;
     stage = stage == 2 ? 0 : stage + 1;
   }
+  // The last iteration's loads (zeros for a tile past the end) must land before the stages
+  // are reused.
+  __builtin_amdgcn_s_waitcnt(kWaitFlags);
+  __syncthreads();
   return over;
 }
 
@@ -539,8 +632,10 @@ __device__ inline void store_rows(const Args &a, const f32x16 (&o)[kQB][D / 32],
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   __shared__ Smem<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);  // known to the compiler as wave-uniform (scalar)
   const int col = lane & 31, half = lane >> 5;
   const int G = a.group;
   const int g = int(blockIdx.x % unsigned(a.hkv));
@@ -634,6 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
     store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
   }
+#endif
 }
 
 template <int D>
