@@ -29,6 +29,25 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
+# HBM bytes per attention launch, from rocprofv3 FETCH_SIZE (x2, calibrated on a plain 1 GiB copy)
+# plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
+# counted on; a changed kernel reports null until it is counted again.
+MEASURED_TRAFFIC = {
+    2: ("bb52b4daf3c4ed4f0c138f341282aa4c3348b71eacf018fd2400154d9aa523d1", 129724920),
+}
+ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
+
+
+def measured_traffic(number: int):
+    import hashlib
+
+    entry = MEASURED_TRAFFIC.get(number)
+    if entry is None or not os.path.exists(ATTENTION_SOURCE):
+        return None
+    with open(ATTENTION_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return entry[1] if digest == entry[0] else None
+
 
 def attention_flops(cfg, tail_len) -> float:
     n = np.asarray(tail_len, np.float64)
@@ -153,17 +172,18 @@ def main():
     rbytes = readout_bytes(cfg, tables.cand_ids, cfg.n_questions)
     n = cfg.n_questions
     ms_per_step = elapsed * 1e3 / args.steps
+    traffic = measured_traffic(cfg.number)  # HBM bytes per launch, or None
     if cfg.prefix_len > 0:
         achieved = flops / (attn_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "kernel": "prefix_tail_attention_kernel",
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch", "kernel": "prefix_tail_attention_kernel",
                 "work_per_launch": f"{flops:.4e} FLOP"}
     else:
         achieved = abytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
-                "kernel": "prefix_tail_attention_kernel",
+                "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch", "kernel": "prefix_tail_attention_kernel",
                 "work_per_launch": f"{abytes:.4e} B"}
 
     baseline = None

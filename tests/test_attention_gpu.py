@@ -125,3 +125,57 @@ def test_out_of_range_offsets_are_skipped_not_faulted():
         if i == 1:
             continue
         np.testing.assert_array_equal(got[o:o + n], good[o:o + n])
+
+
+def _shift(bits, delta):
+    return synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(bits) + np.float32(delta))
+
+
+def _fill(value, shape):
+    return synth.f32_to_bf16_bits(np.full(shape, value, np.float32))
+
+
+# Score-range extremes. A question's queries of KV group 0 are shifted by +1 and one key of
+# that group is set to a constant c, so that key's score is about c * D * scale above the
+# typical ones (c = 6: ~68 nats, past what the kernel's fixed-reference softmax covers, so its
+# exact two-pass recomputation must take over; c = 3: ~34 nats, inside it). The key sits late
+# in the prefix, early in the prefix, or inside the question's own tail; only some questions are
+# shifted, so shifted and plain rows share workgroups.
+EXTREMES = {
+    "prefix_late_past_headroom": (SMALL["4b_like_small"], "prefix", 650, 6.0),
+    "prefix_late_within_headroom": (SMALL["4b_like_small"], "prefix", 650, 3.0),
+    "prefix_early_peak": (SMALL["4b_like_small"], "prefix", 5, 6.0),
+    "tail_past_headroom": (SMALL["4b_like_small"], "tail", 40, 6.0),
+    "plain_tail_past_headroom": (synth.config(4, n_questions=12, tail_lo=100, tail_hi=200),
+                                 "tail", 130, 6.0),
+    "d64_prefix_past_headroom": (SMALL["d64_group1"], "prefix", 100, 8.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXTREMES))
+def test_score_range_extremes(name):
+    cfg, where, pos, c = EXTREMES[name]
+    print(f"attention score extremes: {name}", flush=True)
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    ts = {k: v.copy() for k, v in req.tensors.items()}
+    group = cfg.n_heads_q // cfg.n_heads_kv
+    off = req.pack["token_offset"]
+    shifted = [i for i in range(len(req.tail_len))
+               if i % 2 == 0 and (where == "prefix" or req.tail_len[i] > pos)]
+    assert shifted
+    for i in shifted:
+        rows = slice(off[i], off[i] + int(req.tail_len[i]))
+        ts["q"][rows, :group] = _shift(ts["q"][rows, :group], 1.0)
+        if where == "tail":
+            ts["k_tail"][off[i] + pos, 0] = _fill(c, cfg.head_dim)
+    if where == "prefix":
+        ts["k_prefix"][pos, 0] = _fill(c, cfg.head_dim)
+    got = run_attention(req, tensors=ts)
+    ref = attention_full(ts["q"], ts["k_tail"], ts["v_tail"], ts.get("k_prefix"),
+                         ts.get("v_prefix"), off, req.tail_len, cfg.n_heads_q, cfg.n_heads_kv,
+                         cfg.scale)
+    rows = valid_rows(req)
+    assert np.isfinite(got[rows]).all()
+    err = np.abs(got[rows] - ref[rows]).max()
+    print(f"  max abs err {err:.3e} over {rows.size} rows", flush=True)
+    assert err <= ATTN_TOL
