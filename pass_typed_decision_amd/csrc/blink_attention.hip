@@ -62,13 +62,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;
+constexpr int kThreads = 768;
+constexpr int kWaves = 12;
 constexpr int kQB = 1;                               // 32-row query blocks per wave
 constexpr int kRowsPerWave = 32 * kQB;               // 32
 constexpr int kRowsPerUnit = kWaves * kRowsPerWave;  // 256
 constexpr int kTileKeys = 64;
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kMaxGroup = 16;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
@@ -119,16 +119,17 @@ struct Smem {
   int overflow;  // some row of the workgroup exceeded its reference by more than kHeadroom
 };
 
-// Waits until at most one tile's loads of this wave are in flight (the newest tile's), or none.
-template <int D>
-__device__ inline void wait_tile_loads(int wave, bool keep_one) {
+// Waits until at most `keep` tiles' loads of this wave (the newest ones) are in flight.
+template <int D, int KEEP>
+__device__ inline void wait_tile_loads(int wave) {
   using L = Layout<D>;
-  if (!keep_one)
+  static_assert(KEEP * (L::FULL + 1) < 16, "the vmcnt field used here holds 0..15");
+  if (KEEP == 0)
     __builtin_amdgcn_s_waitcnt(kWaitFlags);
   else if (L::EXTRA > 0 && wave < L::EXTRA)
-    __builtin_amdgcn_s_waitcnt(kWaitFlags | (L::FULL + 1));
+    __builtin_amdgcn_s_waitcnt(kWaitFlags | (KEEP * (L::FULL + 1)));
   else
-    __builtin_amdgcn_s_waitcnt(kWaitFlags | L::FULL);
+    __builtin_amdgcn_s_waitcnt(kWaitFlags | (KEEP * L::FULL));
 }
 
 // Largest q in [0, n) with start[q] <= c (start ascending). Terminates for any contents.
@@ -161,12 +162,10 @@ __device__ inline float pair_sum(float x) {
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 
-// Source of one 64-key tile: rows rowbase + kstart + [0, 64) of k/v, visible below klimit.
+// Source of one 64-key tile: keys [kstart, kstart + 64) of the prefix (q < 0) or of question
+// q's tail (rows rowbase + key of k_tail / v_tail), visible below klimit.
 struct TileSrc {
-  const uint16_t *k;
-  const uint16_t *v;
   int64_t rowbase;
-  int64_t rowcount;  // rows that exist in k/v (bounds check)
   int kstart;
   int klimit;
   int q;  // -1 for the prefix
@@ -213,14 +212,17 @@ struct TileRsrc {
 
 template <int D>
 __device__ inline TileRsrc tile_rsrc(const Args &a, int g, const TileSrc &s) {
+  const bool pre = s.q < 0;
+  const int64_t rowcount = pre ? int64_t(a.prefix_len) : a.t_pad;  // rows that exist
   const int64_t row0 = s.rowbase + s.kstart;
   const int64_t stride = int64_t(a.hkv) * D;  // elements between consecutive rows
   int64_t nkeys = min(int64_t(kTileKeys), int64_t(s.klimit - s.kstart));
-  nkeys = min(nkeys, s.rowcount - row0);
+  nkeys = min(nkeys, rowcount - row0);
   const bool any = s.valid && nkeys > 0 && row0 >= 0;
   const int nbytes = any ? int(((nkeys - 1) * stride + D) * 2) : 0;
   const int64_t first = any ? row0 * stride + int64_t(g) * D : 0;
-  const uint16_t *kb = s.valid ? s.k : nullptr, *vb = s.valid ? s.v : nullptr;
+  const uint16_t *kb = !s.valid ? nullptr : pre ? a.k_pre : a.k_tail;
+  const uint16_t *vb = !s.valid ? nullptr : pre ? a.v_pre : a.v_tail;
   return TileRsrc{
       __builtin_amdgcn_make_buffer_rsrc((void *)(kb + first), (short)0, nbytes, kBufferFlags),
       __builtin_amdgcn_make_buffer_rsrc((void *)(vb + first), (short)0, nbytes, kBufferFlags)};
@@ -451,10 +453,7 @@ __device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const U
     const int limit = (q == u.qz) ? u.posz + 1 : nq;
     // A malformed table cannot make the loop run past the context length.
     if (limit > 0 && limit <= nq && nq <= BLINK_MAX_INPUT_TOKENS) {
-      s.k = a.k_tail;
-      s.v = a.v_tail;
       s.rowbase = a.token_offset[q];
-      s.rowcount = a.t_pad;
       s.kstart = 0;
       s.klimit = limit;
       s.q = q;
@@ -468,10 +467,7 @@ __device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const U
 __device__ inline TileSrc first_tile(const Args &a, const int32_t *start, const Unit &u) {
   if (a.prefix_len > 0) {
     TileSrc s{};
-    s.k = a.k_pre;
-    s.v = a.v_pre;
     s.rowbase = 0;
-    s.rowcount = a.prefix_len;
     s.kstart = 0;
     s.klimit = a.prefix_len;
     s.q = -1;
@@ -509,7 +505,7 @@ __device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], 
   }
 }
 
-// All tiles of the unit through the 3-stage LDS ring; max_only collects exact row maxima.
+// All tiles of the unit through the LDS ring; max_only collects exact row maxima.
 // Returns true when a row of this wave exceeded its reference by more than kHeadroom.
 template <int D>
 __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
@@ -520,22 +516,30 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   const int half = lane >> 5;
   const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
   bool over = false;
-  // Tile t lives in stage t % 3; loads for tile t + 2 are issued before tile t is computed.
-  // The only vector memory operations inside the loop are these tile loads, so waiting for
-  // all but the newest tile's loads (vmcnt) means the previous tile has landed.
+  // Tile t lives in stage t % kStages; loads for tile t + kAhead are issued before tile t is
+  // computed, so kAhead tiles are in flight. The only vector memory operations inside the
+  // loop are these tile loads, so waiting until only the newest kAhead - 1 tiles' loads are
+  // outstanding (vmcnt) means tile t + 1 has landed.
+  constexpr int kAhead = kStages - 1;
+  static_assert(kAhead >= 2, "the ring needs at least three stages");
   TileSrc cur = first;
-  TileSrc nxt = next_tile(a, sm.start, u, cur);
+  TileSrc ahead[kAhead - 1];  // tiles t + 1 .. t + kAhead - 1, whose loads are in flight
+  ahead[0] = next_tile(a, sm.start, u, cur);
+#pragma unroll
+  for (int i = 1; i + 1 < kAhead; ++i) ahead[i] = next_tile(a, sm.start, u, ahead[i - 1]);
   __builtin_amdgcn_sched_barrier(0);
   load_tile_async<D>(tile_rsrc<D>(a, g, cur), sm.k[0], sm.v[0], wave, plan);
-  load_tile_async<D>(tile_rsrc<D>(a, g, nxt), sm.k[1], sm.v[1], wave, plan);
+#pragma unroll
+  for (int i = 0; i + 1 < kAhead; ++i)
+    load_tile_async<D>(tile_rsrc<D>(a, g, ahead[i]), sm.k[i + 1], sm.v[i + 1], wave, plan);
   __builtin_amdgcn_sched_barrier(0);
-  wait_tile_loads<D>(wave, true);
+  wait_tile_loads<D, kAhead - 1>(wave);
   __syncthreads();
   int stage = 0;
   while (true) {
-    // Tile t + 2 (zeros if it does not exist) goes into the stage tile t - 1 used.
-    const TileSrc after = next_tile(a, sm.start, u, nxt);
-    const int stage2 = stage >= 1 ? stage - 1 : 2;  // (stage + 2) % 3
+    // Tile t + kAhead (zeros if it does not exist) goes into the stage tile t - 1 used.
+    const TileSrc after = next_tile(a, sm.start, u, ahead[kAhead - 2]);
+    const int stage2 = stage >= 1 ? stage - 1 : kStages - 1;  // (stage + kAhead) % kStages
     const TileRsrc ra = tile_rsrc<D>(a, g, after);
     __builtin_amdgcn_sched_barrier(0);
     if (Layout<D>::EXTRA > 0 && wave < Layout<D>::EXTRA)
@@ -584,19 +588,21 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
       }
     }
 
-    // This wave's loads of tile t + 1 have landed once only tile t + 2's remain in flight;
-    // the barrier then covers every wave's part.
+    // This wave's loads of tile t + 1 have landed once only the newer tiles' remain in
+    // flight; the barrier then covers every wave's part.
     __builtin_amdgcn_sched_barrier(0);
-    wait_tile_loads<D>(wave, true);
+    wait_tile_loads<D, kAhead - 1>(wave);
     __syncthreads();
-    if (!nxt.valid) break;
-    cur = nxt;
-    nxt = after;
-    stage = stage == 2 ? 0 : stage + 1;
+    if (!ahead[0].valid) break;
+    cur = ahead[0];
+#pragma unroll
+    for (int i = 0; i + 2 < kAhead; ++i) ahead[i] = ahead[i + 1];
+    ahead[kAhead - 2] = after;
+    stage = stage == kStages - 1 ? 0 : stage + 1;
   }
   // The last iteration's loads (zeros for a tile past the end) must land before the stages
   // are reused.
-  __builtin_amdgcn_s_waitcnt(kWaitFlags);
+  wait_tile_loads<D, 0>(wave);
   __syncthreads();
   return over;
 }

@@ -6,12 +6,18 @@
 // and "answer assembly" section, softmax (divide by the temperature, subtract the maximum,
 // exponentiate, normalise) and answer_for (most probable option, earlier option on ties).
 //
-// Design: one workgroup (4 wave64) per question. The hidden row is widened once into
-// registers, each lane owning 16-byte chunks lane, lane+64, ...; every wave streams whole
-// label rows with 16-byte coalesced loads (a 2560-wide bf16 row is five 1 KiB wave loads),
-// two rows at a time for memory-level parallelism, and reduces its partial sums across the
-// wave. Logits go through LDS to wave 0, which does the softmax and argmax. The kernel is
-// bound by HBM bandwidth on the label rows; nothing else is re-read.
+// Design: two launches on the caller's stream.
+//  * label_logits_kernel streams the label rows. Every wave scores up to `rpw` consecutive
+//    options of one question (each question owns ceil(max_options / rpw) wave slots; slots
+//    past its options exit at once), so the work is spread evenly whatever the mix of option
+//    counts (1..255 per question). A wave issues all of its rows' 16-byte coalesced loads at
+//    once (a 2560-wide bf16 row is five 1 KiB wave loads) plus the question's hidden row, then
+//    takes FP32 dot products with v_dot2 (bf16 pairs, FP32 accumulate) and reduces them across
+//    the wave. Blocks are mapped so that each XCD (dispatch is round-robin over the 8 XCDs)
+//    takes one contiguous range of slots, so a question's hidden row is reused in one L2.
+//    The kernel is bound by HBM bandwidth on the label rows.
+//  * label_softmax_kernel: one wave per question over its (at most 255) logits: temperature,
+//    max, exp, sum, normalise, and the first index of the largest logit.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -23,11 +29,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxChunksPerLane = 16;  // d_model <= 16 * 64 * 8 = 8192
+constexpr int kRowChunkBudget = 20;    // 16-byte label chunks in flight per lane
+constexpr int kXcds = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline float wave_sum(float x) {
 #pragma unroll
@@ -41,114 +47,140 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
-template <int NCH>
-__device__ inline float row_dot(const u32x4 (&w)[NCH], const float (&h)[NCH][8]) {
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      acc = fmaf(lo_bf16(w[c][m]), h[c][2 * m], acc);
-      acc = fmaf(hi_bf16(w[c][m]), h[c][2 * m + 1], acc);
-    }
-  }
-  return acc;
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Rows (entries of the flat option list) per wave at most, so that the label chunks in flight
+// stay within the register budget.
 template <int NCH>
-__global__ __launch_bounds__(kThreads) void label_readout_kernel(
+struct Rows {
+  static constexpr int MAX = (kRowChunkBudget / NCH) < 1   ? 1
+                             : (kRowChunkBudget / NCH) > 8 ? 8
+                                                           : kRowChunkBudget / NCH;
+};
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void label_logits_kernel(
     const uint16_t *__restrict__ hidden, int64_t hidden_rows, int d_model,
     const int64_t *__restrict__ last_row, const uint16_t *__restrict__ w_u, int64_t vocab,
-    const int32_t *__restrict__ cand_ids, const int32_t *__restrict__ cand_off,
-    int64_t total_cand, int max_options, float temperature, float *__restrict__ logits,
-    float *__restrict__ probs, int32_t *__restrict__ argmax) {
-  __shared__ float s_z[256];
-  __shared__ int s_bad;
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t *__restrict__ cand_ids, const int32_t *__restrict__ cand_off, int n,
+    int64_t total, int max_options, int rpw, int64_t n_blocks, float *__restrict__ logits) {
+  constexpr int RMAX = Rows<NCH>::MAX;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(int(threadIdx.x >> 6));
 
-  const int64_t lo = cand_off[i], hi = cand_off[i + 1];
-  if (!(lo >= 0 && hi <= total_cand && hi - lo >= 1 && hi - lo <= max_options)) {
-    if (tid == 0) argmax[i] = -1;  // offsets unusable: nothing else can be written safely
-    return;
-  }
-  const int K = int(hi - lo);
-  const int64_t row = last_row[i];
-  const bool row_ok = row >= 0 && row < hidden_rows;
-  if (tid == 0) s_bad = row_ok ? 0 : 1;
+  // Block -> slice of the wave slots: XCD x (= blockIdx % 8) takes blocks [x * per, (x+1) * per),
+  // so one question's slots (and its hidden row) stay on one XCD.
+  const int64_t per = (n_blocks + kXcds - 1) / kXcds;
+  const int64_t blk = int64_t(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (blk >= n_blocks) return;
+  // Every question owns `slots` wave slots of rpw options each; slots past its options idle.
+  const int slots = (max_options + rpw - 1) / rpw;
+  const int64_t ws = blk * kWaves + wave;
+  const int q = int(ws / slots), j = int(ws % slots);
+  if (q >= n) return;
+  const int64_t lo = cand_off[q], hi = cand_off[q + 1];
+  // Unusable offsets: nothing is written here; the softmax kernel flags the question.
+  if (!(lo >= 0 && hi <= total && hi - lo >= 1 && hi - lo <= max_options)) return;
+  const int64_t r0 = lo + int64_t(j) * rpw;
+  if (r0 >= hi) return;
+  const int nr = int(min(int64_t(rpw), hi - r0));
 
+  // This wave's label ids (lane k holds entry r0 + k), then every label row's loads at once,
+  // then the question's hidden row.
+  int32_t my_id = 0;
+  if (lane < nr) my_id = cand_ids[r0 + lane];
+  bool id_ok[RMAX];
+  u32x4 w[RMAX][NCH];
   const int nchunks = d_model >> 3;
-  float h[NCH][8];
-  const uint16_t *hrow = hidden + (row_ok ? row : 0) * int64_t(d_model);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int ch = lane + 64 * c;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (row_ok && ch < nchunks) w = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      h[c][2 * m] = lo_bf16(w[m]);
-      h[c][2 * m + 1] = hi_bf16(w[m]);
-    }
-  }
-  __syncthreads();
-
-  // Two label rows per wave per step: rows k and k + kWaves.
-  for (int k = wave; k < K; k += 2 * kWaves) {
-    const int k2 = k + kWaves;
-    const int32_t id1 = cand_ids[lo + k];
-    const int32_t id2 = k2 < K ? cand_ids[lo + k2] : 0;
-    const bool ok1 = id1 >= 0 && id1 < vocab;
-    const bool ok2 = k2 >= K || (id2 >= 0 && id2 < vocab);
-    const uint16_t *r1 = w_u + int64_t(ok1 ? id1 : 0) * d_model;
-    const uint16_t *r2 = w_u + int64_t(ok2 && k2 < K ? id2 : 0) * d_model;
-    u32x4 w1[NCH], w2[NCH];
+  for (int k = 0; k < RMAX; ++k) {
+    const int32_t id = __builtin_amdgcn_readlane(my_id, k);
+    id_ok[k] = k < nr && id >= 0 && id < vocab;
+    const uint16_t *wrow = w_u + int64_t(id_ok[k] ? id : 0) * d_model;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = lane + 64 * c;
-      w1[c] = u32x4{0u, 0u, 0u, 0u};
-      w2[c] = u32x4{0u, 0u, 0u, 0u};
-      if (ch < nchunks) {
-        w1[c] = *reinterpret_cast<const u32x4 *>(r1 + ch * 8);
-        if (k2 < K) w2[c] = *reinterpret_cast<const u32x4 *>(r2 + ch * 8);
-      }
-    }
-    const float z1 = wave_sum(row_dot<NCH>(w1, h));
-    const float z2 = wave_sum(row_dot<NCH>(w2, h));
-    if (lane == 0) {
-      s_z[k] = z1;
-      if (k2 < K) s_z[k2] = z2;
-      if (!ok1 || !ok2) s_bad = 1;
+      w[k][c] = u32x4{0u, 0u, 0u, 0u};
+      if (k < nr && ch < nchunks) w[k][c] = *reinterpret_cast<const u32x4 *>(wrow + ch * 8);
     }
   }
-  __syncthreads();
-  if (wave != 0) return;
+  const int64_t row = last_row[q];
+  const bool h_ok = row >= 0 && row < hidden_rows;
+  const uint16_t *hrow = hidden + (h_ok ? row : 0) * int64_t(d_model);
+  u32x4 h[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    h[c] = u32x4{0u, 0u, 0u, 0u};
+    if (ch < nchunks) h[c] = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
+  }
 
-  if (s_bad) {
-    for (int k = lane; k < K; k += 64) {
-      logits[lo + k] = __builtin_nanf("");
-      probs[lo + k] = __builtin_nanf("");
+  float z_mine = 0.f;
+#pragma unroll
+  for (int k = 0; k < RMAX; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = dot2(w[k][c][m], h[c][m], acc);
     }
+    const float z = wave_sum(acc);
+    if (lane == k) z_mine = (id_ok[k] && h_ok) ? z : __builtin_nanf("");
+  }
+  if (lane < nr) logits[r0 + lane] = z_mine;
+}
+
+// One wave per question: softmax of the logits divided by the temperature, first-index argmax
+// on the logits. Unusable offsets: argmax -1 and nothing else written; a NaN logit (an id or a
+// hidden row out of range): the question's logits and probabilities become NaN, argmax -1.
+__global__ __launch_bounds__(kThreads) void label_softmax_kernel(
+    const int32_t *__restrict__ cand_off, int n, int64_t total, int max_options,
+    float temperature, float *__restrict__ logits, float *__restrict__ probs,
+    int32_t *__restrict__ argmax) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * kWaves + uniform(int(threadIdx.x >> 6));
+  if (i >= n) return;
+  const int64_t lo = cand_off[i], hi = cand_off[i + 1];
+  if (!(lo >= 0 && hi <= total && hi - lo >= 1 && hi - lo <= max_options)) {
     if (lane == 0) argmax[i] = -1;
     return;
   }
-
-  // Softmax over the question's own options and first-index argmax (on the logits).
-  float zt[4], best = -INFINITY, mt = -INFINITY;
+  const int K = int(hi - lo);
+  float z[4], zt[4], best = -INFINITY, mt = -INFINITY;
   int best_k = K;
+  bool bad = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int k = lane + 64 * j;
+    z[j] = 0.f;
     zt[j] = -INFINITY;
     if (k < K) {
-      const float z = s_z[k];
-      zt[j] = z / temperature;
+      z[j] = logits[lo + k];
+      bad |= isnan(z[j]);
+      zt[j] = z[j] / temperature;
       mt = fmaxf(mt, zt[j]);
-      if (z > best) {  // strict: the earliest k of this lane wins ties
-        best = z;
+      if (z[j] > best) {  // strict: the earliest k of this lane wins ties
+        best = z[j];
         best_k = k;
       }
     }
+  }
+  if (__builtin_amdgcn_ballot_w64(bad)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = lane + 64 * j;
+      if (k < K) {
+        logits[lo + k] = __builtin_nanf("");
+        probs[lo + k] = __builtin_nanf("");
+      }
+    }
+    if (lane == 0) argmax[i] = -1;
+    return;
   }
   mt = wave_max(mt);
 #pragma unroll
@@ -166,33 +198,61 @@ __global__ __launch_bounds__(kThreads) void label_readout_kernel(
     e[j] = (lane + 64 * j < K) ? expf(zt[j] - mt) : 0.f;
     part += e[j];
   }
-  const float total = wave_sum(part);
+  const float sum = wave_sum(part);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int k = lane + 64 * j;
-    if (k < K) {
-      logits[lo + k] = s_z[k];
-      probs[lo + k] = e[j] / total;
-    }
+    if (k < K) probs[lo + k] = e[j] / sum;
   }
   if (lane == 0) argmax[i] = best_k;
 }
 
+struct ReadoutArgs {
+  const uint16_t *hidden;
+  int64_t hidden_rows;
+  int d_model;
+  const int64_t *last_row;
+  const uint16_t *w_u;
+  int64_t vocab;
+  const int32_t *ids;
+  const int32_t *off;
+  int n;
+  int64_t total;
+  int max_options;
+  float temperature;
+  float *logits;
+  float *probs;
+  int32_t *argmax;
+};
+
+// Entries per wave: the most the register budget allows once the list fills the GPU twice
+// over (256 CUs x 16 waves), fewer for short lists so that more waves share them.
+inline int rows_per_wave(int64_t total, int rmax) {
+  const int64_t waves_wanted = 2 * 256 * 16;
+  int64_t r = total / waves_wanted;
+  if (r < 1) r = 1;
+  if (r > rmax) r = rmax;
+  return int(r);
+}
+
 template <int NCH>
-hipError_t launch(const void *hidden, int64_t hidden_rows, int d_model, const int64_t *last_row,
-                  const void *w_u, int64_t vocab, const int32_t *ids, const int32_t *off,
-                  int n, int64_t total, int max_options, float temperature, float *logits,
-                  float *probs, int32_t *argmax, hipStream_t stream) {
-  hipLaunchKernelGGL(label_readout_kernel<NCH>, dim3(n), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t *>(hidden), hidden_rows, d_model, last_row,
-                     static_cast<const uint16_t *>(w_u), vocab, ids, off, total, max_options,
-                     temperature, logits, probs, argmax);
+hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
+  const int rpw = rows_per_wave(a.total, Rows<NCH>::MAX);
+  const int64_t slots = (a.max_options + rpw - 1) / rpw;
+  const int64_t n_blocks = (int64_t(a.n) * slots + kWaves - 1) / kWaves;
+  const int64_t grid = (n_blocks + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(label_logits_kernel<NCH>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                     a.hidden, a.hidden_rows, a.d_model, a.last_row, a.w_u, a.vocab, a.ids,
+                     a.off, a.n, a.total, a.max_options, rpw, n_blocks, a.logits);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(label_softmax_kernel, dim3(unsigned((a.n + kWaves - 1) / kWaves)),
+                     dim3(kThreads), 0, stream, a.off, a.n, a.total, a.max_options,
+                     a.temperature, a.logits, a.probs, a.argmax);
   return hipGetLastError();
 }
 
-typedef hipError_t (*LaunchFn)(const void *, int64_t, int, const int64_t *, const void *, int64_t,
-                               const int32_t *, const int32_t *, int, int64_t, int, float,
-                               float *, float *, int32_t *, hipStream_t);
+typedef hipError_t (*LaunchFn)(const ReadoutArgs &, hipStream_t);
 
 }  // namespace
 
@@ -225,15 +285,16 @@ extern "C" int blink_label_readout(const void *hidden, int64_t hidden_rows, int3
   if (!blink::aligned16(hidden) || !blink::aligned16(w_u))
     return fail(BLINK_E_INVALID, "hidden and w_u must be 16-byte aligned");
 
+  const ReadoutArgs a{static_cast<const uint16_t *>(hidden), hidden_rows, d_model, d_last_row,
+                      static_cast<const uint16_t *>(w_u), vocab, d_cand_ids, d_cand_off,
+                      n_questions, total_candidates, max_options, temperature, d_logits,
+                      d_probs, d_argmax};
   const int nch = (d_model / 8 + 63) / 64;  // 16-byte chunks per lane
   static constexpr LaunchFn fns[] = {launch<1>,  launch<2>,  launch<3>,  launch<4>,
                                      launch<5>,  launch<6>,  launch<7>,  launch<8>,
                                      launch<9>,  launch<10>, launch<11>, launch<12>,
                                      launch<13>, launch<14>, launch<15>, launch<16>};
-  const hipError_t err =
-      fns[nch - 1](hidden, hidden_rows, d_model, d_last_row, w_u, vocab, d_cand_ids, d_cand_off,
-                   n_questions, total_candidates, max_options, temperature, d_logits, d_probs,
-                   d_argmax, static_cast<hipStream_t>(stream));
+  const hipError_t err = fns[nch - 1](a, static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
     return fail(BLINK_E_DEVICE, "blink_label_readout launch: %s", hipGetErrorString(err));
   return blink::ok();
