@@ -6,7 +6,7 @@
 // and "answer assembly" section, softmax (divide by the temperature, subtract the maximum,
 // exponentiate, normalise) and answer_for (most probable option, earlier option on ties).
 //
-// Design: two launches on the caller's stream.
+// Design. Large option tables (bandwidth-bound) take two launches on the caller's stream:
 //  * label_logits_kernel streams the label rows. Every wave scores up to `rpw` consecutive
 //    options of one question (each question owns ceil(max_options / rpw) wave slots; slots
 //    past its options exit at once), so the work is spread evenly whatever the mix of option
@@ -18,6 +18,8 @@
 //    The kernel is bound by HBM bandwidth on the label rows.
 //  * label_softmax_kernel: one wave per question over its (at most 255) logits: temperature,
 //    max, exp, sum, normalise, and the first index of the largest logit.
+// Small tables (launch-latency-bound) take one launch, label_readout_fused_kernel: one
+// workgroup per question scores its rows and finishes it in the same kernel.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -135,32 +137,21 @@ __global__ __launch_bounds__(kThreads) void label_logits_kernel(
   if (lane < nr) logits[r0 + lane] = z_mine;
 }
 
-// One wave per question: softmax of the logits divided by the temperature, first-index argmax
-// on the logits. Unusable offsets: argmax -1 and nothing else written; a NaN logit (an id or a
-// hidden row out of range): the question's logits and probabilities become NaN, argmax -1.
-__global__ __launch_bounds__(kThreads) void label_softmax_kernel(
-    const int32_t *__restrict__ cand_off, int n, int64_t total, int max_options,
-    float temperature, float *__restrict__ logits, float *__restrict__ probs,
-    int32_t *__restrict__ argmax) {
-  const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * kWaves + uniform(int(threadIdx.x >> 6));
-  if (i >= n) return;
-  const int64_t lo = cand_off[i], hi = cand_off[i + 1];
-  if (!(lo >= 0 && hi <= total && hi - lo >= 1 && hi - lo <= max_options)) {
-    if (lane == 0) argmax[i] = -1;
-    return;
-  }
-  const int K = int(hi - lo);
-  float z[4], zt[4], best = -INFINITY, mt = -INFINITY;
+// One wave finishes question i from its K logits (lane holds options lane + 64 j): softmax of
+// the logits divided by the temperature and the first index of the largest logit. A NaN logit
+// (an id or a hidden row out of range) makes the question's logits and probabilities NaN and
+// its argmax -1. Logits are written only when `write_logits` (they may already be in place).
+__device__ inline void finish_question(const float (&z)[4], int K, int lane, float temperature,
+                                       int64_t lo, bool write_logits, float *__restrict__ logits,
+                                       float *__restrict__ probs, int32_t *__restrict__ argmax_i) {
+  float zt[4], best = -INFINITY, mt = -INFINITY;
   int best_k = K;
   bool bad = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int k = lane + 64 * j;
-    z[j] = 0.f;
     zt[j] = -INFINITY;
     if (k < K) {
-      z[j] = logits[lo + k];
       bad |= isnan(z[j]);
       zt[j] = z[j] / temperature;
       mt = fmaxf(mt, zt[j]);
@@ -179,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void label_softmax_kernel(
         probs[lo + k] = __builtin_nanf("");
       }
     }
-    if (lane == 0) argmax[i] = -1;
+    if (lane == 0) *argmax_i = -1;
     return;
   }
   mt = wave_max(mt);
@@ -202,9 +193,108 @@ __global__ __launch_bounds__(kThreads) void label_softmax_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int k = lane + 64 * j;
-    if (k < K) probs[lo + k] = e[j] / sum;
+    if (k < K) {
+      if (write_logits) logits[lo + k] = z[j];
+      probs[lo + k] = e[j] / sum;
+    }
   }
-  if (lane == 0) argmax[i] = best_k;
+  if (lane == 0) *argmax_i = best_k;
+}
+
+__device__ inline bool offsets_usable(int64_t lo, int64_t hi, int64_t total, int max_options) {
+  return lo >= 0 && hi <= total && hi - lo >= 1 && hi - lo <= max_options;
+}
+
+// Second launch of the streaming path: one wave per question over the logits just written.
+// Unusable offsets: argmax -1 and nothing else written.
+__global__ __launch_bounds__(kThreads) void label_softmax_kernel(
+    const int32_t *__restrict__ cand_off, int n, int64_t total, int max_options,
+    float temperature, float *__restrict__ logits, float *__restrict__ probs,
+    int32_t *__restrict__ argmax) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * kWaves + uniform(int(threadIdx.x >> 6));
+  if (i >= n) return;
+  const int64_t lo = cand_off[i], hi = cand_off[i + 1];
+  if (!offsets_usable(lo, hi, total, max_options)) {
+    if (lane == 0) argmax[i] = -1;
+    return;
+  }
+  const int K = int(hi - lo);
+  float z[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = (lane + 64 * j < K) ? logits[lo + lane + 64 * j] : 0.f;
+  finish_question(z, K, lane, temperature, lo, false, logits, probs, argmax + i);
+}
+
+// Small option tables (launch latency, not bandwidth, bounds them): one workgroup per
+// question, its waves taking the question's label rows two at a time, wave 0 finishing.
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void label_readout_fused_kernel(
+    const uint16_t *__restrict__ hidden, int64_t hidden_rows, int d_model,
+    const int64_t *__restrict__ last_row, const uint16_t *__restrict__ w_u, int64_t vocab,
+    const int32_t *__restrict__ cand_ids, const int32_t *__restrict__ cand_off, int64_t total,
+    int max_options, float temperature, float *__restrict__ logits, float *__restrict__ probs,
+    int32_t *__restrict__ argmax) {
+  __shared__ float s_z[BLINK_MAX_OPTIONS + 1];
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(int(threadIdx.x >> 6));
+  const int64_t lo = cand_off[i], hi = cand_off[i + 1];
+  if (!offsets_usable(lo, hi, total, max_options)) {  // uniform across the workgroup
+    if (threadIdx.x == 0) argmax[i] = -1;
+    return;
+  }
+  const int K = int(hi - lo);
+  const int64_t row = last_row[i];
+  const bool h_ok = row >= 0 && row < hidden_rows;
+  const uint16_t *hrow = hidden + (h_ok ? row : 0) * int64_t(d_model);
+  const int nchunks = d_model >> 3;
+  u32x4 h[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    h[c] = u32x4{0u, 0u, 0u, 0u};
+    if (ch < nchunks) h[c] = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
+  }
+  for (int k = wave; k < K; k += 2 * kWaves) {  // rows k and k + kWaves
+    const int k2 = k + kWaves;
+    const bool two = k2 < K;
+    const int32_t id1 = cand_ids[lo + k];
+    const int32_t id2 = two ? cand_ids[lo + k2] : 0;
+    const bool ok1 = id1 >= 0 && id1 < vocab, ok2 = id2 >= 0 && id2 < vocab;
+    const uint16_t *r1 = w_u + int64_t(ok1 ? id1 : 0) * d_model;
+    const uint16_t *r2 = w_u + int64_t(ok2 ? id2 : 0) * d_model;
+    u32x4 w1[NCH], w2[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      w1[c] = u32x4{0u, 0u, 0u, 0u};
+      w2[c] = u32x4{0u, 0u, 0u, 0u};
+      if (ch < nchunks) {
+        w1[c] = *reinterpret_cast<const u32x4 *>(r1 + ch * 8);
+        if (two) w2[c] = *reinterpret_cast<const u32x4 *>(r2 + ch * 8);
+      }
+    }
+    float acc1 = 0.f, acc2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc1 = dot2(w1[c][m], h[c][m], acc1);
+        acc2 = dot2(w2[c][m], h[c][m], acc2);
+      }
+    const float z1 = wave_sum(acc1), z2 = wave_sum(acc2);
+    if (lane == 0) {
+      s_z[k] = (ok1 && h_ok) ? z1 : __builtin_nanf("");
+      if (two) s_z[k2] = (ok2 && h_ok) ? z2 : __builtin_nanf("");
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float z[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = (lane + 64 * j < K) ? s_z[lane + 64 * j] : 0.f;
+  finish_question(z, K, lane, temperature, lo, true, logits, probs, argmax + i);
 }
 
 struct ReadoutArgs {
@@ -235,8 +325,20 @@ inline int rows_per_wave(int64_t total, int rmax) {
   return int(r);
 }
 
+// Below this many bytes of label rows the readout is bound by launch latency: one fused
+// launch beats two (the streaming path pays off on large option tables, where questions with
+// many options would otherwise serialise on one workgroup each).
+constexpr int64_t kFusedMaxBytes = int64_t(32) << 20;
+
 template <int NCH>
 hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
+  if (a.total * a.d_model * 2 <= kFusedMaxBytes) {
+    hipLaunchKernelGGL(label_readout_fused_kernel<NCH>, dim3(unsigned(a.n)), dim3(kThreads), 0,
+                       stream, a.hidden, a.hidden_rows, a.d_model, a.last_row, a.w_u, a.vocab,
+                       a.ids, a.off, a.total, a.max_options, a.temperature, a.logits, a.probs,
+                       a.argmax);
+    return hipGetLastError();
+  }
   const int rpw = rows_per_wave(a.total, Rows<NCH>::MAX);
   const int64_t slots = (a.max_options + rpw - 1) / rpw;
   const int64_t n_blocks = (int64_t(a.n) * slots + kWaves - 1) / kWaves;

@@ -40,16 +40,24 @@ def test_full_size(number):
     _check(req, logits, probs, arg)
 
 
-def test_one_and_255_options():
-    cfg = synth.config(2, n_questions=3)
+# Small tables take the fused one-launch kernel; large ones (over 32 MiB of label rows) the
+# streaming kernel plus a softmax kernel. Both must meet the same bar on the same edge cases.
+@pytest.mark.parametrize("repeat", [1, 30], ids=["fused", "streaming"])
+def test_one_and_255_options(repeat):
+    cfg = synth.config(2, n_questions=3 * repeat)
     req = Request(cfg, parts=READOUT_PARTS)
     rng = np.random.default_rng(5)
-    ids = np.concatenate([rng.choice(cfg.vocab, 1, replace=False),
-                          rng.choice(cfg.vocab, 255, replace=False),
-                          rng.choice(cfg.vocab, 7, replace=False)]).astype(np.int32)
-    off = np.array([0, 1, 256, 263], np.int32)
+    ids, counts = [], []
+    for _ in range(repeat):
+        for k in (1, 255, 7):
+            ids.append(rng.choice(cfg.vocab, k, replace=False))
+            counts.append(k)
+    ids = np.concatenate(ids).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    assert (len(ids) * cfg.d_model * 2 > 32 << 20) == (repeat > 1)
     logits, probs, arg = run_readout(req, cand_ids=ids, cand_off=off)
-    assert probs[0] == 1.0 and arg[0] == 0
+    for i in range(0, len(counts), 3):
+        assert probs[off[i]] == 1.0 and arg[i] == 0
     _check(req, logits, probs, arg, ids=ids, off=off)
 
 
@@ -71,20 +79,26 @@ def test_shared_label_table():
     _check(req, logits, probs, arg, ids=ids)
 
 
-def test_malformed_entries_are_flagged():
-    cfg = synth.config(1)
+@pytest.mark.parametrize("number", [1, 4], ids=["fused", "streaming"])
+def test_malformed_entries_are_flagged(number):
+    cfg = synth.config(number)
     req = Request(cfg, parts=READOUT_PARTS)
     ids = req.tables.cand_ids.copy()
     ids[req.tables.cand_off[1]] = cfg.vocab + 5  # question 1: id out of range
     last = np.asarray(req.pack["last_row"], np.int64).copy()
     last[2] = -3  # question 2: row out of range
+    assert (len(ids) * cfg.d_model * 2 > 32 << 20) == (number == 4)
     logits, probs, arg = run_readout(req, cand_ids=ids, last_row=last)
     off = req.tables.cand_off
     assert arg[1] == -1 and arg[2] == -1
     assert np.isnan(probs[off[1]:off[2]]).all() and np.isnan(probs[off[2]:off[3]]).all()
-    good = [0, 3]
+    assert np.isnan(logits[off[1]:off[2]]).all() and np.isnan(logits[off[2]:off[3]]).all()
     z, p, a = label_readout(req.tensors["hidden"], req.pack["last_row"], req.tensors["w_u"],
                             req.tables.cand_ids, off, cfg.temperature)
+    good = [0] + list(range(3, len(off) - 1))
     for i in good:
         np.testing.assert_allclose(probs[off[i]:off[i + 1]], p[off[i]:off[i + 1]], atol=PROB_TOL)
-        assert arg[i] == a[i]
+        np.testing.assert_allclose(logits[off[i]:off[i + 1]], z[off[i]:off[i + 1]], atol=LOGIT_TOL)
+    sub_off = np.concatenate([[0], np.cumsum([off[i + 1] - off[i] for i in good])])
+    sub = np.concatenate([np.arange(off[i], off[i + 1]) for i in good])
+    check_argmax(z[sub], sub_off, a[good], arg[good])
