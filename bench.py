@@ -152,15 +152,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        p = step.pack_and_upload()
+        total_valid = step.pack_and_upload()
         ev[i][0].record(stream)
-        step.attention(p)
+        step.attention(total_valid)
         ev[i][1].record(stream)
         step.readout()
         ev[i][2].record(stream)
-        with torch.cuda.stream(stream):
-            step.h_probs.copy_(step.probs, non_blocking=True)
-            step.h_argmax.copy_(step.argmax, non_blocking=True)
+        step.download()
         stream.synchronize()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0

@@ -113,6 +113,28 @@ class Pack:
     total_valid_tokens: int
 
 
+def pack_ragged_args(tail_len, prefix_len, token_budget, max_rows, order, batch_of, row_of,
+                     token_offset, last_row, valid_start, batch_first, batch_width, batch_base,
+                     n_batches, total_padded, total_valid) -> list:
+    """Argument list of blink_pack_ragged over caller-owned arrays (which must stay alive
+    and keep their sizes) and ctypes scalars for the three counts; for repeated calls."""
+    t = tail_len
+    n = int(t.shape[0])
+    arrays = ((t, np.int32, n), (order, np.int32, n), (batch_of, np.int32, n),
+              (row_of, np.int32, n), (token_offset, np.int64, n), (last_row, np.int64, n),
+              (valid_start, np.int32, n + 1), (batch_first, np.int32, n + 1),
+              (batch_width, np.int32, n), (batch_base, np.int64, n + 1))
+    for a, dt, size in arrays:
+        if a.dtype != dt or not a.flags["C_CONTIGUOUS"] or a.shape[0] < size:
+            raise BlinkError(BLINK_E_INVALID, "pack buffers have the wrong type or size")
+    c32, c64 = ctypes.c_int32, ctypes.c_int64
+    return [_ptr(t, c32), n, int(prefix_len), int(token_budget), int(max_rows),
+            _ptr(order, c32), _ptr(batch_of, c32), _ptr(row_of, c32), _ptr(token_offset, c64),
+            _ptr(last_row, c64), _ptr(valid_start, c32), _ptr(batch_first, c32),
+            _ptr(batch_width, c32), _ptr(batch_base, c64), ctypes.byref(n_batches),
+            ctypes.byref(total_padded), ctypes.byref(total_valid)]
+
+
 def pack_ragged(tail_len, prefix_len: int = 0, token_budget: int = TOKEN_BUDGET,
                 max_rows: int = 0) -> Pack:
     """Host packer (blink_pack_ragged)."""
@@ -167,10 +189,12 @@ def _dev(t, dtype, name):
 
 
 def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offset,
-                          valid_start, total_valid_tokens: int, scale: float, stream=None):
+                          valid_start, total_valid_tokens: int, scale: float, stream=None,
+                          launch: bool = True):
     """Launches blink_prefix_tail_attention. Shapes: q/out [T_pad, H_q, D], k/v_tail
     [T_pad, H_kv, D], k/v_prefix [P, H_kv, D] or None; token_offset int64 [n],
-    valid_start int32 [n + 1] (device)."""
+    valid_start int32 [n + 1] (device). With ``launch=False`` returns the checked argument
+    list instead (index 9 is total_valid_tokens) for repeated launches."""
     import torch
 
     bf = torch.bfloat16
@@ -193,18 +217,22 @@ def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offs
     if int(valid_start.shape[0]) != n + 1:
         raise BlinkError(BLINK_E_INVALID, "valid_start must have n + 1 entries")
     lib = load_library()
-    _check(lib.blink_prefix_tail_attention(
+    args = [
         _dev(q, bf, "q"), _dev(k_tail, bf, "k_tail"), _dev(v_tail, bf, "v_tail"), kp, vp,
         _dev(out, bf, "out"), _dev(token_offset, torch.int64, "token_offset"),
         _dev(valid_start, torch.int32, "valid_start"), n, int(total_valid_tokens), int(t_pad),
-        p, int(hq), int(hkv), int(d), float(scale), _stream(stream)))
+        p, int(hq), int(hkv), int(d), float(scale), _stream(stream)]
+    if not launch:
+        return args
+    _check(lib.blink_prefix_tail_attention(*args))
 
 
 def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
-                  max_options: int, logits, probs, argmax, stream=None):
+                  max_options: int, logits, probs, argmax, stream=None, launch: bool = True):
     """Launches blink_label_readout. hidden [T_pad, d_model] bf16, last_row int64 [n],
     w_u [vocab, d_model] bf16, cand_ids int32 [sum K], cand_off int32 [n + 1];
-    outputs logits/probs float32 [sum K], argmax int32 [n] (device)."""
+    outputs logits/probs float32 [sum K], argmax int32 [n] (device). With ``launch=False``
+    returns the checked argument list instead, for repeated launches."""
     import torch
 
     bf = torch.bfloat16
@@ -217,13 +245,16 @@ def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
     if int(logits.shape[0]) != total or int(probs.shape[0]) != total or int(argmax.shape[0]) != n:
         raise BlinkError(BLINK_E_INVALID, "output sizes do not match the candidate table")
     lib = load_library()
-    _check(lib.blink_label_readout(
+    args = [
         _dev(hidden, bf, "hidden"), int(hidden.shape[0]), int(hidden.shape[1]),
         _dev(last_row, torch.int64, "last_row"), _dev(w_u, bf, "w_u"), int(w_u.shape[0]),
         _dev(cand_ids, torch.int32, "cand_ids"), _dev(cand_off, torch.int32, "cand_off"), n, total,
         int(max_options), float(temperature), _dev(logits, torch.float32, "logits"),
         _dev(probs, torch.float32, "probs"), _dev(argmax, torch.int32, "argmax"),
-        _stream(stream)))
+        _stream(stream)]
+    if not launch:
+        return args
+    _check(lib.blink_label_readout(*args))
 
 
 def check_candidate_table(cand_ids, cand_off, vocab: int) -> int:

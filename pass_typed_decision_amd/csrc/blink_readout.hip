@@ -7,15 +7,15 @@
 // exponentiate, normalise) and answer_for (most probable option, earlier option on ties).
 //
 // Design. Large option tables (bandwidth-bound) take two launches on the caller's stream:
-//  * label_logits_kernel streams the label rows. Every wave scores up to `rpw` consecutive
-//    options of one question (each question owns ceil(max_options / rpw) wave slots; slots
-//    past its options exit at once), so the work is spread evenly whatever the mix of option
-//    counts (1..255 per question). A wave issues all of its rows' 16-byte coalesced loads at
-//    once (a 2560-wide bf16 row is five 1 KiB wave loads) plus the question's hidden row, then
-//    takes FP32 dot products with v_dot2 (bf16 pairs, FP32 accumulate) and reduces them across
-//    the wave. Blocks are mapped so that each XCD (dispatch is round-robin over the 8 XCDs)
-//    takes one contiguous range of slots, so a question's hidden row is reused in one L2.
-//    The kernel is bound by HBM bandwidth on the label rows.
+//  * label_logits_flat_kernel streams the label rows: the options of all questions form one
+//    flat list (the CSR order of cand_ids) and every wave scores one entry of it, so the work
+//    is spread evenly whatever the mix of option counts (1..255 per question). A wave loads
+//    its label row with 16-byte coalesced loads (a 2560-wide bf16 row is five 1 KiB wave
+//    loads) while the workgroup stages the question offsets in LDS; a binary search there
+//    names the question, whose hidden row (shared by many waves, so an L2 hit) then gives the
+//    FP32 dot product (v_dot2: bf16 pairs, FP32 accumulate), reduced across the wave. Blocks
+//    are mapped so that each XCD (dispatch is round-robin over the 8 XCDs) takes one
+//    contiguous slice of the list. The kernel is bound by HBM bandwidth on the label rows.
 //  * label_softmax_kernel: one wave per question over its (at most 255) logits: temperature,
 //    max, exp, sum, normalise, and the first index of the largest logit.
 // Small tables (launch-latency-bound) take one launch, label_readout_fused_kernel: one
@@ -31,7 +31,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxChunksPerLane = 16;  // d_model <= 16 * 64 * 8 = 8192
-constexpr int kRowChunkBudget = 20;    // 16-byte label chunks in flight per lane
 constexpr int kXcds = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -56,85 +55,64 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Rows (entries of the flat option list) per wave at most, so that the label chunks in flight
-// stay within the register budget.
-template <int NCH>
-struct Rows {
-  static constexpr int MAX = (kRowChunkBudget / NCH) < 1   ? 1
-                             : (kRowChunkBudget / NCH) > 8 ? 8
-                                                           : kRowChunkBudget / NCH;
-};
+constexpr int kFlatWaves = 16;
+
+// Question owning flat entry r: the last i in [0, n) with off[i] <= r (off staged in LDS).
+__device__ inline int owner_of(const int32_t *s_off, int n, int64_t r) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (int64_t(s_off[mid]) <= r)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
 
 template <int NCH>
-__global__ __launch_bounds__(kThreads) void label_logits_kernel(
+__global__ __launch_bounds__(64 * kFlatWaves) void label_logits_flat_kernel(
     const uint16_t *__restrict__ hidden, int64_t hidden_rows, int d_model,
     const int64_t *__restrict__ last_row, const uint16_t *__restrict__ w_u, int64_t vocab,
     const int32_t *__restrict__ cand_ids, const int32_t *__restrict__ cand_off, int n,
-    int64_t total, int max_options, int rpw, int64_t n_blocks, float *__restrict__ logits) {
-  constexpr int RMAX = Rows<NCH>::MAX;
+    int64_t total, int64_t n_blocks, float *__restrict__ logits) {
+  __shared__ int32_t s_off[BLINK_MAX_QUESTIONS + 1];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(int(threadIdx.x >> 6));
-
-  // Block -> slice of the wave slots: XCD x (= blockIdx % 8) takes blocks [x * per, (x+1) * per),
-  // so one question's slots (and its hidden row) stay on one XCD.
   const int64_t per = (n_blocks + kXcds - 1) / kXcds;
   const int64_t blk = int64_t(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
   if (blk >= n_blocks) return;
-  // Every question owns `slots` wave slots of rpw options each; slots past its options idle.
-  const int slots = (max_options + rpw - 1) / rpw;
-  const int64_t ws = blk * kWaves + wave;
-  const int q = int(ws / slots), j = int(ws % slots);
-  if (q >= n) return;
-  const int64_t lo = cand_off[q], hi = cand_off[q + 1];
-  // Unusable offsets: nothing is written here; the softmax kernel flags the question.
-  if (!(lo >= 0 && hi <= total && hi - lo >= 1 && hi - lo <= max_options)) return;
-  const int64_t r0 = lo + int64_t(j) * rpw;
-  if (r0 >= hi) return;
-  const int nr = int(min(int64_t(rpw), hi - r0));
-
-  // This wave's label ids (lane k holds entry r0 + k), then every label row's loads at once,
-  // then the question's hidden row.
-  int32_t my_id = 0;
-  if (lane < nr) my_id = cand_ids[r0 + lane];
-  bool id_ok[RMAX];
-  u32x4 w[RMAX][NCH];
+  const int64_t r = blk * kFlatWaves + wave;
+  const bool live = r < total;
+  const int32_t id = live ? cand_ids[r] : 0;  // scalar: uniform address
+  for (int i = threadIdx.x; i <= n; i += 64 * kFlatWaves) s_off[i] = cand_off[i];
+  const bool id_ok = id >= 0 && id < vocab;
+  const uint16_t *wrow = w_u + int64_t(id_ok ? id : 0) * d_model;
   const int nchunks = d_model >> 3;
-#pragma unroll
-  for (int k = 0; k < RMAX; ++k) {
-    const int32_t id = __builtin_amdgcn_readlane(my_id, k);
-    id_ok[k] = k < nr && id >= 0 && id < vocab;
-    const uint16_t *wrow = w_u + int64_t(id_ok[k] ? id : 0) * d_model;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ch = lane + 64 * c;
-      w[k][c] = u32x4{0u, 0u, 0u, 0u};
-      if (k < nr && ch < nchunks) w[k][c] = *reinterpret_cast<const u32x4 *>(wrow + ch * 8);
-    }
-  }
-  const int64_t row = last_row[q];
-  const bool h_ok = row >= 0 && row < hidden_rows;
-  const uint16_t *hrow = hidden + (h_ok ? row : 0) * int64_t(d_model);
-  u32x4 h[NCH];
+  u32x4 w[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int ch = lane + 64 * c;
-    h[c] = u32x4{0u, 0u, 0u, 0u};
-    if (ch < nchunks) h[c] = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
+    w[c] = u32x4{0u, 0u, 0u, 0u};
+    if (live && ch < nchunks) w[c] = *reinterpret_cast<const u32x4 *>(wrow + ch * 8);
   }
-
-  float z_mine = 0.f;
+  __syncthreads();
+  if (!live) return;
+  const int q = uniform(owner_of(s_off, n, r));
+  const int64_t row = last_row[q];
+  const bool h_ok = row >= 0 && row < hidden_rows;
+  const uint16_t *hrow = hidden + (h_ok ? row : 0) * int64_t(d_model);
+  float acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < RMAX; ++k) {
-    float acc = 0.f;
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    u32x4 h = u32x4{0u, 0u, 0u, 0u};
+    if (ch < nchunks) h = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) acc = dot2(w[k][c][m], h[c][m], acc);
-    }
-    const float z = wave_sum(acc);
-    if (lane == k) z_mine = (id_ok[k] && h_ok) ? z : __builtin_nanf("");
+    for (int m = 0; m < 4; ++m) acc = dot2(w[c][m], h[m], acc);
   }
-  if (lane < nr) logits[r0 + lane] = z_mine;
+  const float z = wave_sum(acc);
+  if (lane == 0) logits[r] = (id_ok && h_ok) ? z : __builtin_nanf("");
 }
 
 // One wave finishes question i from its K logits (lane holds options lane + 64 j): softmax of
@@ -315,16 +293,6 @@ struct ReadoutArgs {
   int32_t *argmax;
 };
 
-// Entries per wave: the most the register budget allows once the list fills the GPU twice
-// over (256 CUs x 16 waves), fewer for short lists so that more waves share them.
-inline int rows_per_wave(int64_t total, int rmax) {
-  const int64_t waves_wanted = 2 * 256 * 16;
-  int64_t r = total / waves_wanted;
-  if (r < 1) r = 1;
-  if (r > rmax) r = rmax;
-  return int(r);
-}
-
 // Below this many bytes of label rows the readout is bound by launch latency: one fused
 // launch beats two (the streaming path pays off on large option tables, where questions with
 // many options would otherwise serialise on one workgroup each).
@@ -339,13 +307,11 @@ hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
                        a.argmax);
     return hipGetLastError();
   }
-  const int rpw = rows_per_wave(a.total, Rows<NCH>::MAX);
-  const int64_t slots = (a.max_options + rpw - 1) / rpw;
-  const int64_t n_blocks = (int64_t(a.n) * slots + kWaves - 1) / kWaves;
+  const int64_t n_blocks = (a.total + kFlatWaves - 1) / kFlatWaves;
   const int64_t grid = (n_blocks + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(label_logits_kernel<NCH>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                     a.hidden, a.hidden_rows, a.d_model, a.last_row, a.w_u, a.vocab, a.ids,
-                     a.off, a.n, a.total, a.max_options, rpw, n_blocks, a.logits);
+  hipLaunchKernelGGL(label_logits_flat_kernel<NCH>, dim3(unsigned(grid)), dim3(64 * kFlatWaves),
+                     0, stream, a.hidden, a.hidden_rows, a.d_model, a.last_row, a.w_u, a.vocab,
+                     a.ids, a.off, a.n, a.total, n_blocks, a.logits);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(label_softmax_kernel, dim3(unsigned((a.n + kWaves - 1) / kWaves)),

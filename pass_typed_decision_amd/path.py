@@ -19,7 +19,9 @@ from ._binding import (
     BLINK_E_INVALID,
     check_candidate_table,
     label_readout,
+    load_library,
     pack_ragged,
+    pack_ragged_args,
     prefix_tail_attention,
     TOKEN_BUDGET,
 )
@@ -37,16 +39,23 @@ def label_name(index: int) -> str:
 
 
 class ScoringStep:
-    """Device-resident request plus reusable buffers; ``run()`` is one scoring step."""
+    """Device-resident request plus reusable buffers; ``run()`` is one scoring step.
+
+    Everything that does not change between steps is prepared once: the packer writes the
+    row tables straight into one pinned buffer that a single copy uploads, the launches use
+    argument lists validated at construction, and the probabilities and argmax share one
+    device buffer that a single copy brings back."""
 
     def __init__(self, tail_len, cand_ids, cand_off, tensors: dict, n_heads_q: int,
                  n_heads_kv: int, prefix_len: int, temperature: float, scale: float,
                  token_budget: int = TOKEN_BUDGET, max_rows: int = 0, stream=None):
+        import ctypes
+
         import torch
 
         self.torch = torch
         self.tail_len = np.ascontiguousarray(np.asarray(tail_len, np.int32))
-        self.n = int(self.tail_len.shape[0])
+        n = self.n = int(self.tail_len.shape[0])
         self.prefix_len = int(prefix_len)
         self.token_budget = int(token_budget)
         self.max_rows = int(max_rows)
@@ -64,55 +73,90 @@ class ScoringStep:
         self.cand_ids = torch.as_tensor(np.asarray(cand_ids, np.int32)).to(dev)
         self.cand_off = torch.as_tensor(np.asarray(cand_off, np.int32)).to(dev)
         total = int(self.cand_ids.shape[0])
-        pin = dict(pin_memory=True)
-        self.h_token_offset = torch.zeros(self.n, dtype=torch.int64, **pin)
-        self.h_last_row = torch.zeros(self.n, dtype=torch.int64, **pin)
-        self.h_valid_start = torch.zeros(self.n + 1, dtype=torch.int32, **pin)
-        self.d_token_offset = torch.zeros(self.n, dtype=torch.int64, device=dev)
-        self.d_last_row = torch.zeros(self.n, dtype=torch.int64, device=dev)
-        self.d_valid_start = torch.zeros(self.n + 1, dtype=torch.int32, device=dev)
+
+        # Row tables, host (pinned) and device, in one buffer each: token_offset int64 [n],
+        # last_row int64 [n], valid_start int32 [n + 1].
+        words = 2 * n + (n + 2) // 2
+        self.h_tab = torch.zeros(words, dtype=torch.int64, pin_memory=True)
+        self.d_tab = torch.zeros(words, dtype=torch.int64, device=dev)
+        tab = self.h_tab.numpy()
+        self.h_token_offset, self.h_last_row = tab[:n], tab[n:2 * n]
+        self.h_valid_start = tab[2 * n:].view(np.int32)[:n + 1]
+        self.d_token_offset, self.d_last_row = self.d_tab[:n], self.d_tab[n:2 * n]
+        self.d_valid_start = self.d_tab[2 * n:].view(torch.int32)[:n + 1]
+        # The packer's other outputs (host only).
+        self._order, self._batch_of, self._row_of = (np.zeros(n, np.int32) for _ in range(3))
+        self._batch_first = np.zeros(n + 1, np.int32)
+        self._batch_width = np.zeros(n, np.int32)
+        self._batch_base = np.zeros(n + 1, np.int64)
+        self._nb, self._tp, self._tv = ctypes.c_int32(0), ctypes.c_int64(0), ctypes.c_int64(0)
+
         t_pad = pk.total_padded_tokens
         self.out = torch.empty(t_pad, n_heads_q, tensors["q"].shape[2], dtype=torch.bfloat16,
                                device=dev)
         self.logits = torch.empty(total, dtype=torch.float32, device=dev)
-        self.probs = torch.empty(total, dtype=torch.float32, device=dev)
-        self.argmax = torch.empty(self.n, dtype=torch.int32, device=dev)
-        self.h_probs = torch.empty(total, dtype=torch.float32, **pin)
-        self.h_argmax = torch.empty(self.n, dtype=torch.int32, **pin)
+        # Probabilities and argmax in one buffer (float32 [total] then int32 [n]).
+        self.d_res = torch.empty(total + n, dtype=torch.float32, device=dev)
+        self.probs, self.argmax = self.d_res[:total], self.d_res[total:].view(torch.int32)
+        self.h_res = torch.empty(total + n, dtype=torch.float32, pin_memory=True)
+        self.h_probs, self.h_argmax = self.h_res[:total], self.h_res[total:].view(torch.int32)
 
-    def pack_and_upload(self):
-        pk = pack_ragged(self.tail_len, self.prefix_len, self.token_budget, self.max_rows)
-        self.h_token_offset.numpy()[:] = pk.token_offset
-        self.h_last_row.numpy()[:] = pk.last_row
-        self.h_valid_start.numpy()[:] = pk.valid_start
+        # Argument lists checked once; every step reuses them.
+        lib = load_library()
+        self._pack_fn = lib.blink_pack_ragged
+        self._pack_args = pack_ragged_args(
+            self.tail_len, self.prefix_len, self.token_budget, self.max_rows, self._order,
+            self._batch_of, self._row_of, self.h_token_offset, self.h_last_row,
+            self.h_valid_start, self._batch_first, self._batch_width, self._batch_base,
+            self._nb, self._tp, self._tv)
+        t = tensors
+        self._attn_fn = lib.blink_prefix_tail_attention
+        self._attn_args = prefix_tail_attention(
+            t["q"], t["k_tail"], t["v_tail"], t.get("k_prefix"), t.get("v_prefix"), self.out,
+            self.d_token_offset, self.d_valid_start, pk.total_valid_tokens, self.scale,
+            stream=self.stream.cuda_stream, launch=False)
+        self._read_fn = lib.blink_label_readout
+        self._read_args = label_readout(
+            t["hidden"], self.d_last_row, t["w_u"], self.cand_ids, self.cand_off,
+            self.temperature, self.max_options, self.logits, self.probs, self.argmax,
+            stream=self.stream.cuda_stream, launch=False)
+
+    @staticmethod
+    def _call(fn, args):
+        rc = fn(*args)
+        if rc != 0:
+            raise BlinkError(rc, load_library().blink_last_error().decode("utf-8", "replace"))
+
+    def pack_and_upload(self) -> int:
+        """Packs the tails into the pinned tables and queues their upload (one copy);
+        returns the number of real tail tokens."""
+        self._call(self._pack_fn, self._pack_args)
+        if self._tp.value != self.pack.total_padded_tokens:
+            raise BlinkError(BLINK_E_INVALID, "tensors were not laid out for this pack")
         with self.torch.cuda.stream(self.stream):
-            self.d_token_offset.copy_(self.h_token_offset, non_blocking=True)
-            self.d_last_row.copy_(self.h_last_row, non_blocking=True)
-            self.d_valid_start.copy_(self.h_valid_start, non_blocking=True)
-        return pk
+            self.d_tab.copy_(self.h_tab, non_blocking=True)
+        return self._tv.value
 
-    def attention(self, pk):
-        t = self.t
-        prefix_tail_attention(t["q"], t["k_tail"], t["v_tail"], t.get("k_prefix"),
-                              t.get("v_prefix"), self.out, self.d_token_offset,
-                              self.d_valid_start, pk.total_valid_tokens, self.scale,
-                              stream=self.stream.cuda_stream)
+    def attention(self, total_valid: int):
+        self._attn_args[9] = int(total_valid)
+        self._call(self._attn_fn, self._attn_args)
 
     def readout(self):
-        label_readout(self.t["hidden"], self.d_last_row, self.t["w_u"], self.cand_ids,
-                      self.cand_off, self.temperature, self.max_options, self.logits,
-                      self.probs, self.argmax, stream=self.stream.cuda_stream)
+        self._call(self._read_fn, self._read_args)
+
+    def download(self):
+        """Queues the copy of probabilities and argmax to pinned host memory."""
+        with self.torch.cuda.stream(self.stream):
+            self.h_res.copy_(self.d_res, non_blocking=True)
 
     def run(self, fetch: bool = True):
         """One step. With ``fetch`` the probabilities and argmax are copied to pinned host
         memory and the stream is synchronised; returns (probs, argmax) host arrays."""
-        pk = self.pack_and_upload()
-        self.attention(pk)
+        total_valid = self.pack_and_upload()
+        self.attention(total_valid)
         self.readout()
         if not fetch:
             return None
-        with self.torch.cuda.stream(self.stream):
-            self.h_probs.copy_(self.probs, non_blocking=True)
-            self.h_argmax.copy_(self.argmax, non_blocking=True)
+        self.download()
         self.stream.synchronize()
         return self.h_probs.numpy(), self.h_argmax.numpy()

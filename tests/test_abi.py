@@ -74,6 +74,39 @@ def test_pack_matches_oracle_random(blink):
         np.testing.assert_array_equal(pk.valid_start, vs)
 
 
+def test_prepared_pack_call_matches_pack_ragged(blink):
+    # The scoring step calls the packer through a prepared argument list that writes the
+    # row tables into one shared buffer (int64 offsets, int64 last rows, int32 starts).
+    import ctypes
+
+    from pass_typed_decision_amd._binding import pack_ragged_args
+
+    rng = np.random.default_rng(7)
+    lib = blink.load_library()
+    for _ in range(200):
+        n = int(rng.integers(1, 513))
+        lengths = rng.integers(1, int(rng.choice([5, 300, 4000])) + 1, size=n).astype(np.int32)
+        budget, max_rows = int(rng.choice([64, 32768])), int(rng.choice([0, 3]))
+        tab = np.full(2 * n + (n + 2) // 2, -7, np.int64)
+        offs, last, vs = tab[:n], tab[n:2 * n], tab[2 * n:].view(np.int32)[:n + 1]
+        extra = [np.zeros(n, np.int32) for _ in range(3)] + [
+            np.zeros(n + 1, np.int32), np.zeros(n, np.int32), np.zeros(n + 1, np.int64)]
+        nb, tp, tv = ctypes.c_int32(0), ctypes.c_int64(0), ctypes.c_int64(0)
+        args = pack_ragged_args(lengths, 0, budget, max_rows, extra[0], extra[1], extra[2], offs,
+                                last, vs, extra[3], extra[4], extra[5], nb, tp, tv)
+        assert lib.blink_pack_ragged(*args) == 0
+        pk = blink.pack_ragged(lengths, 0, budget, max_rows)
+        np.testing.assert_array_equal(offs, pk.token_offset)
+        np.testing.assert_array_equal(last, pk.last_row)
+        np.testing.assert_array_equal(vs, pk.valid_start)
+        np.testing.assert_array_equal(extra[0], pk.order)
+        assert (nb.value, tp.value, tv.value) == (
+            pk.n_batches, pk.total_padded_tokens, pk.total_valid_tokens)
+    with pytest.raises(blink.BlinkError):
+        pack_ragged_args(lengths, 0, budget, max_rows, extra[0], extra[1], extra[2],
+                         offs.astype(np.int32), last, vs, extra[3], extra[4], extra[5], nb, tp, tv)
+
+
 @pytest.mark.parametrize("lengths, prefix, code, msg", [
     ([], 0, -2, "0 questions; supported 1-512"),
     ([1] * 513, 0, -2, "513 questions; supported 1-512"),
