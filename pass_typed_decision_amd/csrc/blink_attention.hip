@@ -7,19 +7,24 @@
 // tail row at position t sees every prefix key and the question's tail keys 0..t.
 //
 // Kernel design (one launch for every question of the request):
-//  * Work unit = one KV head g and 256 consecutive "query rows" of that head's group, where
+//  * Work unit = one KV head g and 384 consecutive "query rows" of that head's group, where
 //    the rows are (real tail token, query head of the group) pairs, token-major, over all
 //    questions in question order. Padding rows are never computed, and a unit may span
 //    question boundaries, so a launch has no ragged-tile waste except at its very end.
-//  * Workgroup = 8 wave64, two per SIMD; each wave owns 32 query rows. Two waves per SIMD let
-//    the hardware overlap one wave's softmax (vector ALU) with the other's matrix work. Every
+//  * Workgroup = 12 wave64, three per SIMD; each wave owns 32 query rows. Every K/V tile
+//    brought from L2 feeds all 384 rows, which keeps the L2-to-CU traffic per FLOP low (at
+//    256 rows per tile it alone cost a third of the run time), and three waves per SIMD let the
+//    hardware overlap one wave's softmax (vector ALU) with the others' matrix work. Every
 //    32x32x16 MFMA consumes 1 KiB of LDS fragment data, so the four SIMDs of a CU need
 //    128 B/clk at the full MFMA rate, below the ~200 B/clk the LDS sustains for the
 //    (bank-conflict-free) access patterns used here.
 //  * K/V tiles of 64 keys go straight from global memory into LDS (buffer loads with the LDS
-//    destination; no staging registers), in a 3-stage ring so two tiles are in flight while
-//    one is computed. The buffer descriptor's record count covers exactly the keys that are
-//    visible for the tile, so the hardware zero-fills everything past them.
+//    destination; no staging registers) in a 4-stage ring worked in pairs: while tiles t and
+//    t + 1 are computed, tiles t + 2 and t + 3 load into the other two stages, and one wait
+//    plus one workgroup barrier per pair (not per tile) publishes them; waves that run ahead
+//    within a pair do not wait for the slowest one at every tile. The buffer descriptor's
+//    record count covers exactly the keys that are visible for the tile, so the hardware
+//    zero-fills everything past them.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: in the
 //    accumulator layout a lane holds one query and 16 keys of each 32-key block, so row max and
 //    row sum are lane-local except for one exchange with the partner lane (l ^ 32). The
@@ -65,8 +70,8 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kThreads = 768;
 constexpr int kWaves = 12;
 constexpr int kQB = 1;                               // 32-row query blocks per wave
-constexpr int kRowsPerWave = 32 * kQB;               // 32
-constexpr int kRowsPerUnit = kWaves * kRowsPerWave;  // 256
+constexpr int kRowsPerWave = 32 * kQB;
+constexpr int kRowsPerUnit = kWaves * kRowsPerWave;  // 384
 constexpr int kTileKeys = 64;
 constexpr int kStages = 4;
 constexpr int kMaxGroup = 16;
@@ -119,18 +124,9 @@ struct Smem {
   int overflow;  // some row of the workgroup exceeded its reference by more than kHeadroom
 };
 
-// Waits until at most `keep` tiles' loads of this wave (the newest ones) are in flight.
-template <int D, int KEEP>
-__device__ inline void wait_tile_loads(int wave) {
-  using L = Layout<D>;
-  static_assert(KEEP * (L::FULL + 1) < 16, "the vmcnt field used here holds 0..15");
-  if (KEEP == 0)
-    __builtin_amdgcn_s_waitcnt(kWaitFlags);
-  else if (L::EXTRA > 0 && wave < L::EXTRA)
-    __builtin_amdgcn_s_waitcnt(kWaitFlags | (KEEP * (L::FULL + 1)));
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitFlags | (KEEP * L::FULL));
-}
+// Waits until this wave's tile loads have all landed. They are the only vector memory
+// operations of the tile loop, so a zero vector-memory count means exactly that.
+__device__ inline void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(kWaitFlags); }
 
 // Largest q in [0, n) with start[q] <= c (start ascending). Terminates for any contents.
 __device__ inline int find_question(const int32_t *start, int n, int64_t c) {
@@ -505,7 +501,7 @@ __device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], 
   }
 }
 
-// All tiles of the unit through the LDS ring; max_only collects exact row maxima.
+// All tiles of the unit through the 4-stage LDS ring; max_only collects exact row maxima.
 // Returns true when a row of this wave exceeded its reference by more than kHeadroom.
 template <int D>
 __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
@@ -516,30 +512,24 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   const int half = lane >> 5;
   const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
   bool over = false;
-  // Tile t lives in stage t % kStages; loads for tile t + kAhead are issued before tile t is
-  // computed, so kAhead tiles are in flight. The only vector memory operations inside the
-  // loop are these tile loads, so waiting until only the newest kAhead - 1 tiles' loads are
-  // outstanding (vmcnt) means tile t + 1 has landed.
-  constexpr int kAhead = kStages - 1;
-  static_assert(kAhead >= 2, "the ring needs at least three stages");
+  // Tiles go in pairs (2t, 2t + 1) -> stages (0, 1) or (2, 3). While a pair is computed, the
+  // next pair is loaded into the other two stages; one wait for all loads plus one barrier at
+  // the end of each pair makes the next pair visible and frees this one's stages.
+  static_assert(kStages == 4, "pairs of tiles in a 4-stage ring");
   TileSrc cur = first;
-  TileSrc ahead[kAhead - 1];  // tiles t + 1 .. t + kAhead - 1, whose loads are in flight
-  ahead[0] = next_tile(a, sm.start, u, cur);
-#pragma unroll
-  for (int i = 1; i + 1 < kAhead; ++i) ahead[i] = next_tile(a, sm.start, u, ahead[i - 1]);
+  TileSrc nxt = next_tile(a, sm.start, u, cur);  // tile t + 1
   __builtin_amdgcn_sched_barrier(0);
   load_tile_async<D>(tile_rsrc<D>(a, g, cur), sm.k[0], sm.v[0], wave, plan);
-#pragma unroll
-  for (int i = 0; i + 1 < kAhead; ++i)
-    load_tile_async<D>(tile_rsrc<D>(a, g, ahead[i]), sm.k[i + 1], sm.v[i + 1], wave, plan);
+  load_tile_async<D>(tile_rsrc<D>(a, g, nxt), sm.k[1], sm.v[1], wave, plan);
   __builtin_amdgcn_sched_barrier(0);
-  wait_tile_loads<D, kAhead - 1>(wave);
+  wait_tile_loads();
   __syncthreads();
+  TileSrc nxt2 = next_tile(a, sm.start, u, nxt);  // tile t + 2: the next pair's first
   int stage = 0;
   while (true) {
-    // Tile t + kAhead (zeros if it does not exist) goes into the stage tile t - 1 used.
-    const TileSrc after = next_tile(a, sm.start, u, ahead[kAhead - 2]);
-    const int stage2 = stage >= 1 ? stage - 1 : kStages - 1;  // (stage + kAhead) % kStages
+    // Tile t + 2 goes into the stage of tile t - 2 (the previous pair, done before the barrier).
+    const TileSrc after = nxt2;
+    const int stage2 = stage ^ 2;
     const TileRsrc ra = tile_rsrc<D>(a, g, after);
     __builtin_amdgcn_sched_barrier(0);
     if (Layout<D>::EXTRA > 0 && wave < Layout<D>::EXTRA)
@@ -588,21 +578,19 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
       }
     }
 
-    // This wave's loads of tile t + 1 have landed once only the newer tiles' remain in
-    // flight; the barrier then covers every wave's part.
     __builtin_amdgcn_sched_barrier(0);
-    wait_tile_loads<D, kAhead - 1>(wave);
-    __syncthreads();
-    if (!ahead[0].valid) break;
-    cur = ahead[0];
-#pragma unroll
-    for (int i = 0; i + 2 < kAhead; ++i) ahead[i] = ahead[i + 1];
-    ahead[kAhead - 2] = after;
-    stage = stage == kStages - 1 ? 0 : stage + 1;
+    if (stage & 1) {  // end of a pair: the next pair has landed for every wave
+      wait_tile_loads();
+      __syncthreads();
+    }
+    if (!nxt.valid) break;
+    cur = nxt;
+    nxt = nxt2;
+    nxt2 = next_tile(a, sm.start, u, nxt2);
+    stage = (stage + 1) & 3;
   }
-  // The last iteration's loads (zeros for a tile past the end) must land before the stages
-  // are reused.
-  wait_tile_loads<D, 0>(wave);
+  // The last loads (zeros for tiles past the end) must land before the stages are reused.
+  wait_tile_loads();
   __syncthreads();
   return over;
 }
