@@ -41,8 +41,10 @@
 //    accumulator directly, and probabilities may grow up to 2^64 above the reference (FP32
 //    and bf16 hold that with room to spare), so the O accumulators are never rescaled inside
 //    the loop. Should any row's scores exceed its reference by more than that (extreme
-//    inputs only), the workgroup recomputes exactly: one pass for the exact row maxima, then
-//    the normal pass with m fixed at them. Row sums are taken over the bf16-rounded
+//    inputs only), its sum of probabilities ends above 2^64 (or inf or NaN), which one check
+//    per row at the end of the unit catches (the full-tile path itself takes no row maxima),
+//    and the workgroup recomputes exactly: one pass for the exact row maxima, then the normal
+//    pass with m fixed at them. Row sums are taken over the bf16-rounded
 //    probabilities that the PV product uses (v_dot2 with ones). Nothing a row computes depends
 //    on which other rows share its wave.
 //  * Prefix tiles first (unmasked except the last partial tile), then the tail tiles of each
@@ -77,6 +79,7 @@ constexpr int kStages = 4;
 constexpr int kMaxGroup = 16;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
+constexpr float kSumLimit = 0x1p64f;            // 2^kHeadroom: largest row sum a pass accepts
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3 (32-bit data)
 constexpr int kWaitFlags = 0xF70;               // s_waitcnt with expcnt/lgkmcnt at their max
 
@@ -382,7 +385,7 @@ __device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
 // The next tile's FULL regular loads are issued between the score MFMAs, one per 4 MFMAs, so
 // the waves of a CU do not all queue their loads at once after the barrier.
 template <int D>
-__device__ inline bool compute_tile_fast(const char *kt, const char *vt,
+__device__ inline void compute_tile_fast(const char *kt, const char *vt,
                                          bf16x8 (&qf)[kQB][D / 16], f32x16 (&o)[kQB][D / 32],
                                          RowState (&rs)[kQB], const TileRsrc &load_src,
                                          char *next_k, char *next_v, int wave,
@@ -420,21 +423,15 @@ __device__ inline bool compute_tile_fast(const char *kt, const char *vt,
     if (step % 4 == 3 && step / 4 < Layout<D>::FULL)
       __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
   }
-  bool over = false;
+  // No row maximum here: a probability above 2^kHeadroom shows up in the row sum, which the
+  // kernel checks once at the end of the unit.
   bf16x8 pb[2][kQB][2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float m = s[sub][qb][0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[sub][qb][v]);
-      over |= pair_max(m) > kHeadroom;
-      probs_to_bf16(s[sub][qb], 0.0f, pb[sub][qb], rs[qb].l);
-    }
+    for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[sub][qb], 0.0f, pb[sub][qb], rs[qb].l);
     pv_product<D>(vt, 32 * sub, pb[sub], o);
   }
-  return over;
 }
 
 struct Unit {
@@ -545,8 +542,8 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     const bool fast = !max_only && cur.q < 0 && cur.kstart + kTileKeys <= a.prefix_len &&
                       !__builtin_amdgcn_ballot_w64(fresh);
     if (active && fast) {
-      over |= compute_tile_fast<D>(sm.k[stage] + klane, sm.v[stage] + vlane, qf, o, rs, ra,
-                                   sm.k[stage2], sm.v[stage2], wave, plan);
+      compute_tile_fast<D>(sm.k[stage] + klane, sm.v[stage] + vlane, qf, o, rs, ra,
+                           sm.k[stage2], sm.v[stage2], wave, plan);
     } else {
 #pragma unroll
       for (int i = 0; i < Layout<D>::FULL; ++i)
@@ -707,8 +704,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
   init_rows<D>(o, rs, true);
-  const bool over =
+  bool over =
       run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
+  // Any probability above 2^kHeadroom (or an inf or NaN) leaves its row sum above 2^kHeadroom.
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) over |= rvalid[qb] && !(pair_sum(rs[qb].l) <= kSumLimit);
   store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
   // Did any wave of the workgroup overflow? (The flag was cleared before the first barrier.)
   if (__builtin_amdgcn_ballot_w64(over)) sm.overflow = 1;
