@@ -124,7 +124,7 @@ struct Smem {
   __attribute__((aligned(16))) char k[kStages][Layout<D>::KBYTES];
   __attribute__((aligned(16))) char v[kStages][Layout<D>::VBYTES];
   int32_t start[BLINK_MAX_QUESTIONS + 1];
-  int overflow;  // some row of the workgroup exceeded its reference by more than kHeadroom
+  int overflow;  // some row of the workgroup ended with a sum of probabilities above 2^kHeadroom
 };
 
 // Waits until this wave's tile loads have all landed. They are the only vector memory
@@ -309,9 +309,8 @@ __device__ inline void pv_product(const char *vt, int key0, const bf16x8 (&pb)[k
 
 // kt/vt point at the tile plus this lane's part of the fragment addresses.
 // MAX_ONLY: only the row maxima are taken (raw scores, log2 units) for the exact pass.
-// Returns true when some row of this wave exceeded its reference by more than kHeadroom.
 template <int D, bool MAX_ONLY>
-__device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
+__device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
                                        bf16x8 (&qf)[kQB][D / 16],
                                        f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB],
                                        bool masked, const int (&lim)[kQB]) {
@@ -341,33 +340,34 @@ __device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
       }
     }
   }
-  float mx[kQB];
-  bool fresh_any = false, over = false;
+  if (MAX_ONLY) {
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    float m = s[qb][0];
+    for (int qb = 0; qb < kQB; ++qb) {
+      float m = s[qb][0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) m = fmaxf(m, s[qb][v]);
-    mx[qb] = pair_max(m);
-    if (MAX_ONLY) {
-      rs[qb].m = fmaxf(rs[qb].m, mx[qb]);
-    } else if (rs[qb].m == -INFINITY) {
-      fresh_any |= mx[qb] > -INFINITY;
-    } else {
-      over |= mx[qb] > kHeadroom;
+      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[qb][v]);
+      rs[qb].m = fmaxf(rs[qb].m, pair_max(m));
     }
+    return;
   }
-  if (MAX_ONLY) return false;
-
+  // Row maxima are needed only to set the reference of rows that have none yet (a score far
+  // above a reference shows up in the row sum, which the kernel checks at the end).
+  bool no_ref = false;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) no_ref |= rs[qb].m == -INFINITY;
   bf16x8 pb[kQB][2];
-  if (__builtin_amdgcn_ballot_w64(fresh_any)) {
+  if (__builtin_amdgcn_ballot_w64(no_ref)) {
     // First visible keys of some row: its reference becomes this tile's max (its O and l
     // are still zero). Other rows subtract 0, bit-identical to the common path.
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const bool fresh = rs[qb].m == -INFINITY && mx[qb] > -INFINITY;
-      const float delta = fresh ? mx[qb] : 0.0f;
-      if (fresh) rs[qb].m = mx[qb];
+      float m = s[qb][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[qb][v]);
+      const float mx = pair_max(m);
+      const bool fresh = rs[qb].m == -INFINITY && mx > -INFINITY;
+      const float delta = fresh ? mx : 0.0f;
+      if (fresh) rs[qb].m = mx;
       probs_to_bf16(s[qb], delta, pb[qb], rs[qb].l);
     }
   } else {
@@ -375,13 +375,12 @@ __device__ inline bool compute_subtile(const char *kt, const char *vt, int key0,
     for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[qb], 0.0f, pb[qb], rs[qb].l);
   }
   pv_product<D>(vt, key0, pb, o);
-  return over;
 }
 
 // A full, unmasked 64-key tile for a wave whose rows all have their reference already (the
 // common case: every prefix tile after the first). Both 32-key score blocks are computed
 // first, all in one basic block, so one block's softmax (vector ALU) can be interleaved with
-// the other block's matrix products. Returns true when a row exceeded its headroom.
+// the other block's matrix products.
 // The next tile's FULL regular loads are issued between the score MFMAs, one per 4 MFMAs, so
 // the waves of a CU do not all queue their loads at once after the barrier.
 template <int D>
@@ -499,16 +498,14 @@ __device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], 
 }
 
 // All tiles of the unit through the 4-stage LDS ring; max_only collects exact row maxima.
-// Returns true when a row of this wave exceeded its reference by more than kHeadroom.
 template <int D>
-__device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
+__device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
                                  const TileSrc &first, const RowTables &rt, const WaveSpan &ws,
                                  int klane, int vlane, int wave, int lane,
                                  bf16x8 (&qf)[kQB][D / 16], f32x16 (&o)[kQB][D / 32],
                                  RowState (&rs)[kQB], bool max_only) {
   const int half = lane >> 5;
   const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
-  bool over = false;
   // Tiles go in pairs (2t, 2t + 1) -> stages (0, 1) or (2, 3). While a pair is computed, the
   // next pair is loaded into the other two stages; one wait for all loads plus one barrier at
   // the end of each pair makes the next pair visible and frees this one's stages.
@@ -571,7 +568,7 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
         if (max_only)
           compute_subtile<D, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
         else
-          over |= compute_subtile<D, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+          compute_subtile<D, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
       }
     }
 
@@ -589,7 +586,6 @@ __device__ inline bool run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   // The last loads (zeros for tiles past the end) must land before the stages are reused.
   wait_tile_loads();
   __syncthreads();
-  return over;
 }
 
 // Normalise and store bf16 rows (four consecutive dims per 8-byte store).
@@ -704,9 +700,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
   init_rows<D>(o, rs, true);
-  bool over =
-      run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
+  run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
   // Any probability above 2^kHeadroom (or an inf or NaN) leaves its row sum above 2^kHeadroom.
+  bool over = false;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) over |= rvalid[qb] && !(pair_sum(rs[qb].l) <= kSumLimit);
   store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
