@@ -498,24 +498,33 @@ __device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], 
 }
 
 // All tiles of the unit through the 4-stage LDS ring; max_only collects exact row maxima.
+// Issues the ring's first pair of tiles (stages 0 and 1).
+template <int D>
+__device__ inline void start_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
+                                   const TileSrc &first, int wave, const LoadPlan<D> &plan) {
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile_async<D>(tile_rsrc<D>(a, g, first), sm.k[0], sm.v[0], wave, plan);
+  load_tile_async<D>(tile_rsrc<D>(a, g, next_tile(a, sm.start, u, first)), sm.k[1], sm.v[1],
+                     wave, plan);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// `started`: start_tiles has been called (its loads may still be in flight).
 template <int D>
 __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int g,
                                  const TileSrc &first, const RowTables &rt, const WaveSpan &ws,
                                  int klane, int vlane, int wave, int lane,
-                                 bf16x8 (&qf)[kQB][D / 16], f32x16 (&o)[kQB][D / 32],
-                                 RowState (&rs)[kQB], bool max_only) {
+                                 const LoadPlan<D> &plan, bf16x8 (&qf)[kQB][D / 16],
+                                 f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], bool max_only,
+                                 bool started) {
   const int half = lane >> 5;
-  const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
   // Tiles go in pairs (2t, 2t + 1) -> stages (0, 1) or (2, 3). While a pair is computed, the
   // next pair is loaded into the other two stages; one wait for all loads plus one barrier at
   // the end of each pair makes the next pair visible and frees this one's stages.
   static_assert(kStages == 4, "pairs of tiles in a 4-stage ring");
   TileSrc cur = first;
   TileSrc nxt = next_tile(a, sm.start, u, cur);  // tile t + 1
-  __builtin_amdgcn_sched_barrier(0);
-  load_tile_async<D>(tile_rsrc<D>(a, g, cur), sm.k[0], sm.v[0], wave, plan);
-  load_tile_async<D>(tile_rsrc<D>(a, g, nxt), sm.k[1], sm.v[1], wave, plan);
-  __builtin_amdgcn_sched_barrier(0);
+  if (!started) start_tiles<D>(a, sm, u, g, first, wave, plan);
   wait_tile_loads();
   __syncthreads();
   TileSrc nxt2 = next_tile(a, sm.start, u, nxt);  // tile t + 2: the next pair's first
@@ -550,7 +559,7 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     if (active && !fast) {
       const char *kt = sm.k[stage] + klane;
       const char *vt = sm.v[stage] + vlane;
-#pragma unroll 1
+#pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int base = cur.kstart + 32 * sub;  // first key of the sub-tile
         const bool masked = !(cur.q < 0 && base + 32 <= a.prefix_len);
@@ -654,6 +663,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     wposz = uniform(int(cz - sm.start[wqz]));
   }
 
+  // The ring's first pair of K/V tiles goes out before the query rows are fetched, so the
+  // two latencies overlap.
+  const TileSrc first = first_tile(a, sm.start, u);
+  if (!first.valid) return;  // uniform: nothing visible (cannot happen for a valid table)
+  const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
+  start_tiles<D>(a, sm, u, g, first, wave, plan);
+
   // This lane's query rows: Q pre-scaled by scale * log2(e), rounded to bf16 once.
   bool rvalid[kQB];
   int rq[kQB], rpos[kQB], rhead[kQB];
@@ -692,15 +708,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const int klane = col * Layout<D>::KRS + 16 * half;
   const int vlane = v_lane_offset<D>(lane);
 
-  const TileSrc first = first_tile(a, sm.start, u);
-  if (!first.valid) return;  // uniform: nothing visible (cannot happen for a valid table)
-
   const RowTables rt{rq, rpos};
   const WaveSpan ws{wave_active, wqa, wqz, wposz};
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
   init_rows<D>(o, rs, true);
-  run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
+  run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
+               true);
   // Any probability above 2^kHeadroom (or an inf or NaN) leaves its row sum above 2^kHeadroom.
   bool over = false;
 #pragma unroll
@@ -714,9 +728,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     // its rows overwrite the ones just stored. (The accumulators are reused: the stored values
     // are dead, so nothing has to be merged.)
     init_rows<D>(o, rs, true);
-    run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, true);
+    run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, true,
+                 false);
     init_rows<D>(o, rs, false);
-    run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, qf, o, rs, false);
+    run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
+                 false);
     store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
   }
 #endif
