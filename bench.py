@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
 # counted on; a changed kernel reports null until it is counted again.
 MEASURED_TRAFFIC = {
-    2: ("72e0ca1555a0e5128a1ffb84d0b23d5e8310fb67c183aad9652ba20a7de9b3d7", 131676328),
+    2: ("67eb015a758d66cedbbc9dbfa612086c22760c201df2ba25ddfb4570d2ed0b82", 130552696),
 }
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 
