@@ -391,6 +391,9 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
                                          const LoadPlan<D> &plan) {
   constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
   constexpr int kSteps = 2 * (D / 16);  // score MFMA steps (each kQB MFMAs) in the tile
+  // Raised wave priority for the score MFMAs: the SIMD issues this wave's matrix burst ahead
+  // of the other waves' softmax vector work, so the matrix pipe stays fed (measured: +3 to +6%).
+  __builtin_amdgcn_s_setprio(1);
   f32x16 s[2][kQB];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
@@ -414,6 +417,7 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
         issue_load<D>(load_src, next_k, next_v, wave, plan, step / 4);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   // Keep that order: K fragment read, its MFMAs, and a tile load after every fourth step.
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
