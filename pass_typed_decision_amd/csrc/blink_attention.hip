@@ -100,6 +100,8 @@ struct Args {
   int hkv;
   int group;
   float scale_log2;
+  int64_t full_units;  // per KV head: units [0, full_units) hold kRowsPerUnit rows each,
+  int small_rows;      // later units small_rows each (see unit_split)
 };
 
 template <int D>
@@ -646,22 +648,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   __syncthreads();
   const int64_t valid_total = min(int64_t(uniform(sm.start[a.n])), a.total_valid);
   const int64_t R = valid_total * G;
-  const int64_t row0 = unit * kRowsPerUnit;
+  const int64_t row0 = unit < a.full_units
+                           ? unit * kRowsPerUnit
+                           : a.full_units * kRowsPerUnit + (unit - a.full_units) * a.small_rows;
   if (row0 >= R) return;  // uniform across the workgroup
+  const int64_t row_end =
+      min(R, row0 + (unit < a.full_units ? int64_t(kRowsPerUnit) : int64_t(a.small_rows)));
 
   // Questions touched by the workgroup and by this wave.
   Unit u;
   {
-    const int64_t c0 = row0 / G, cz = (min(row0 + kRowsPerUnit, R) - 1) / G;
+    const int64_t c0 = row0 / G, cz = (row_end - 1) / G;
     u.qa = uniform(find_question(sm.start, a.n, c0));
     u.qz = uniform(find_question(sm.start, a.n, cz));
     u.posz = uniform(int(cz - sm.start[u.qz]));
   }
   const int64_t wr0 = row0 + wave * kRowsPerWave;
-  const bool wave_active = wr0 < R;
+  const bool wave_active = wr0 < row_end;
   int wqa = 0, wqz = -1, wposz = -1;
   if (wave_active) {
-    const int64_t c0 = wr0 / G, cz = (min(wr0 + kRowsPerWave, R) - 1) / G;
+    const int64_t c0 = wr0 / G, cz = (min(wr0 + kRowsPerWave, row_end) - 1) / G;
     wqa = uniform(find_question(sm.start, a.n, c0));
     wqz = uniform(find_question(sm.start, a.n, cz));
     wposz = uniform(int(cz - sm.start[wqz]));
@@ -682,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int64_t r = row0 + wave * kRowsPerWave + qb * 32 + col;
-    rvalid[qb] = r < R;
+    rvalid[qb] = r < row_end;
     const int64_t c = rvalid[qb] ? r / G : 0;
     const int hl = int(r % G);
     const int q = find_question(sm.start, a.n, c);
@@ -742,11 +748,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
 #endif
 }
 
+// Work split per KV head (`rows` query rows each) over `cus` compute units, one workgroup per
+// CU at a time. Uniform units of kRowsPerUnit rows leave the last round of workgroups partly
+// empty, yet it lasts a full unit's time. Instead the rows left after the full rounds are
+// spread over every CU of the last round, in units whose waves give each SIMD fewer waves
+// (multiples of 4 waves), so that round ends sooner. Returns the units per head.
+inline int64_t unit_split(int64_t rows, int hkv, int cus, int64_t &full_units, int &small_rows) {
+  const int64_t units = (rows + kRowsPerUnit - 1) / kRowsPerUnit;
+  full_units = units;
+  small_rows = kRowsPerUnit;
+  const int64_t per_round = cus / hkv;  // units of one head in one round
+  if (per_round < 1 || units * hkv <= cus) return units;
+  const int64_t full = units / per_round * per_round;
+  const int64_t rem = rows - full * kRowsPerUnit;
+  if (rem <= 0) return units;
+  const int64_t simd_rows = 4 * kRowsPerWave;  // one wave on each SIMD
+  const int64_t small = (rem + per_round - 1) / per_round;
+  const int64_t small_up = (small + simd_rows - 1) / simd_rows * simd_rows;
+  if (small_up >= kRowsPerUnit) return units;
+  full_units = full;
+  small_rows = int(small_up);
+  return full + (rem + small_up - 1) / small_up;
+}
+
 template <int D>
 hipError_t launch(const Args &a, hipStream_t stream) {
-  const int64_t rows = a.total_valid * a.group;
-  const int64_t units = (rows + kRowsPerUnit - 1) / kRowsPerUnit;
-  const int64_t blocks = units * a.hkv;
+  const int64_t blocks =
+      (a.full_units + (a.total_valid * a.group - a.full_units * kRowsPerUnit + a.small_rows - 1) /
+                          a.small_rows) * a.hkv;
   hipLaunchKernelGGL(prefix_tail_attention_kernel<D>, dim3(unsigned(blocks)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
@@ -789,10 +818,15 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
     return fail(BLINK_E_INVALID, "token totals do not fit: %lld real of %lld padded for %d "
                 "questions", (long long)total_valid_tokens, (long long)total_padded_tokens,
                 n_questions);
-  const int64_t blocks =
-      (total_valid_tokens * (n_heads_q / n_heads_kv) + kRowsPerUnit - 1) / kRowsPerUnit *
-      n_heads_kv;
-  if (blocks > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "launch too large");
+  int device = 0, cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return fail(BLINK_E_DEVICE, "blink_prefix_tail_attention: no device");
+  int64_t full_units = 0;
+  int small_rows = 0;
+  const int64_t units = unit_split(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv,
+                                   cus, full_units, small_rows);
+  if (units * n_heads_kv > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "launch too large");
   const void *ptrs[] = {q, k_tail, v_tail, out, prefix_len ? k_prefix : q,
                         prefix_len ? v_prefix : q};
   for (const void *p : ptrs)
@@ -815,6 +849,8 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
   a.hkv = n_heads_kv;
   a.group = n_heads_q / n_heads_kv;
   a.scale_log2 = scale * kLog2e;
+  a.full_units = full_units;
+  a.small_rows = small_rows;
 
   (void)hipGetLastError();
   const hipError_t err = head_dim == 64 ? launch<64>(a, static_cast<hipStream_t>(stream))
