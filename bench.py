@@ -1,15 +1,17 @@
 """Benchmark of one-pass typed-decision scoring on one MI355X.
 
 A step is the whole hot path over one request: host pack of the question tails, upload of the
-row tables, shared-prefix tail-prefill attention (HIP), label readout (HIP), and the copy of the
-label probabilities and argmax back to the host. Inputs stay resident in HBM between steps.
+row tables, shared-prefix tail-prefill attention (HIP), label readout (HIP) writing the label
+probabilities and argmax into pinned host memory, and the stream synchronisation that hands
+them to the host. Inputs stay resident in HBM between steps.
 
 Default workload: the 4B-like layer slice (32 query / 8 KV heads, head_dim 128, a 2048-token
 shared prefix, 32 questions with 64-256-token tails, readout over vocab 151936 x hidden 2560 with
 2-8 options per question, temperature 1.0), synthetic seeded data.
 
 Prints ONE JSON line (see the "metric" key). The dominant kernel's roofline figure uses HIP
-events recorded on the launch stream around every timed attention launch; the CPU baseline is
+events (without the system-scope fence) recorded on the launch stream around every timed
+attention launch; the CPU baseline is
 the FP64 oracle timed on a bounded sample of the same request.
 """
 
@@ -93,6 +95,46 @@ def cpu_baseline(cfg, req_tables, tensors, budget_s: float):
     }
 
 
+class TimingEvents:
+    """HIP events recorded on the launch stream, created without the system-scope fence: a
+    timing-only event then adds no cache write-back and invalidation between the kernels it
+    brackets (the HIP runtime's own recommendation for events used only to time work)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count: int, stream):
+        import ctypes
+
+        hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+        self.ctypes, self.hip = ctypes, hip
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
+        self.events = []
+        for _ in range(count):
+            ev = ctypes.c_void_p()
+            self._check(hip.hipEventCreateWithFlags(ctypes.byref(ev),
+                                                    ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)))
+            self.events.append(ev)
+
+    @staticmethod
+    def _check(rc):
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed with error {rc}")
+
+    def record(self, i: int):
+        self._check(self.hip.hipEventRecord(self.events[i], self.stream))
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ctypes.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.ctypes.byref(ms), self.events[a],
+                                                 self.events[b]))
+        return ms.value
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,24 +189,23 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = TimingEvents(3 * args.steps, stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         total_valid = step.pack_and_upload()
-        ev[i][0].record(stream)
+        ev.record(3 * i)
         step.attention(total_valid)
-        ev[i][1].record(stream)
+        ev.record(3 * i + 1)
         step.readout()
-        ev[i][2].record(stream)
-        step.download()
+        ev.record(3 * i + 2)
         stream.synchronize()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    read_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    attn_ms = float(np.mean([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]))
+    read_ms = float(np.mean([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]))
+    ev.close()
     flops = attention_flops(cfg, tables.tail_len)
     abytes = attention_bytes(cfg, tables.tail_len)
     rbytes = readout_bytes(cfg, tables.cand_ids, cfg.n_questions)

@@ -152,9 +152,13 @@ int blink_prefix_tail_attention(const void *q, const void *k_tail, const void *v
  *   max_options 1..255: upper bound of every K_i
  *   d_model     multiple of 8, 8..8192
  *   temperature finite and > 0 (else BLINK_E_INVALID, "temperature must be positive")
- *   d_logits, d_probs  float32 [total_candidates] device outputs
- *   d_argmax    int32 [n] device output; -1 (with NaN logits/probs) marks a question whose
+ *   d_logits    float32 [total_candidates] device output
+ *   d_probs     float32 [total_candidates] output
+ *   d_argmax    int32 [n] output; -1 (with NaN logits/probs) marks a question whose
  *               table entries were out of range
+ *               d_probs and d_argmax are only written, never read: each may be device memory
+ *               or pinned host memory the device can access (hipHostMalloc), which the host
+ *               may read once the stream has been synchronised.
  */
 int blink_label_readout(const void *hidden, int64_t hidden_rows, int32_t d_model,
                         const int64_t *d_last_row, const void *w_u, int64_t vocab,

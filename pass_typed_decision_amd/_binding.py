@@ -188,6 +188,17 @@ def _dev(t, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dev_or_pinned(t, dtype, name):
+    """An output the device writes: a device tensor, or pinned host memory it can reach."""
+    import torch
+
+    if isinstance(t, torch.Tensor) and not t.is_cuda and t.is_pinned():
+        if t.dtype != dtype or not t.is_contiguous():
+            raise BlinkError(BLINK_E_INVALID, f"{name} must be contiguous {dtype}")
+        return ctypes.c_void_p(t.data_ptr())
+    return _dev(t, dtype, name)
+
+
 def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offset,
                           valid_start, total_valid_tokens: int, scale: float, stream=None,
                           launch: bool = True):
@@ -231,7 +242,8 @@ def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
                   max_options: int, logits, probs, argmax, stream=None, launch: bool = True):
     """Launches blink_label_readout. hidden [T_pad, d_model] bf16, last_row int64 [n],
     w_u [vocab, d_model] bf16, cand_ids int32 [sum K], cand_off int32 [n + 1];
-    outputs logits/probs float32 [sum K], argmax int32 [n] (device). With ``launch=False``
+    outputs logits float32 [sum K] (device), probs float32 [sum K] and argmax int32 [n] (device,
+    or pinned host memory, readable once the stream is synchronised). With ``launch=False``
     returns the checked argument list instead, for repeated launches."""
     import torch
 
@@ -250,7 +262,8 @@ def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
         _dev(last_row, torch.int64, "last_row"), _dev(w_u, bf, "w_u"), int(w_u.shape[0]),
         _dev(cand_ids, torch.int32, "cand_ids"), _dev(cand_off, torch.int32, "cand_off"), n, total,
         int(max_options), float(temperature), _dev(logits, torch.float32, "logits"),
-        _dev(probs, torch.float32, "probs"), _dev(argmax, torch.int32, "argmax"),
+        _dev_or_pinned(probs, torch.float32, "probs"),
+        _dev_or_pinned(argmax, torch.int32, "argmax"),
         _stream(stream)]
     if not launch:
         return args

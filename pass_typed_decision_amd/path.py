@@ -9,7 +9,9 @@ request's tensors stay resident on the device between steps.
 
 from __future__ import annotations
 
+import ctypes
 import itertools
+import os
 import string
 
 import numpy as np
@@ -32,6 +34,24 @@ _LABELS = list(string.ascii_uppercase) + [
     a + b for a, b in itertools.product(string.ascii_uppercase, repeat=2)]
 
 
+_HIP_MEMCPY_H2D = 1
+
+
+def _hip_memcpy_async():
+    """hipMemcpyAsync of the HIP runtime this process already runs (torch and libblink.so
+    share one copy). Queuing a copy through it avoids torch's stream-context switch, which
+    costs several microseconds per copy on the host."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+    except OSError as exc:
+        raise RuntimeError("the HIP runtime is not loaded in this process") from exc
+    fn = hip.hipMemcpyAsync
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                   ctypes.c_void_p]
+    return fn
+
+
 def label_name(index: int) -> str:
     if not 0 <= index < 255:
         raise BlinkError(BLINK_E_INVALID, f"option index {index} outside 0-254")
@@ -43,8 +63,9 @@ class ScoringStep:
 
     Everything that does not change between steps is prepared once: the packer writes the
     row tables straight into one pinned buffer that a single copy uploads, the launches use
-    argument lists validated at construction, and the probabilities and argmax share one
-    device buffer that a single copy brings back."""
+    argument lists validated at construction, and the readout writes the probabilities and
+    argmax straight into one pinned host buffer. Those host buffers are reused, so a step
+    queued with ``run(fetch=False)`` must be synchronised before the next step is packed."""
 
     def __init__(self, tail_len, cand_ids, cand_off, tensors: dict, n_heads_q: int,
                  n_heads_kv: int, prefix_len: int, temperature: float, scale: float,
@@ -95,14 +116,18 @@ class ScoringStep:
         self.out = torch.empty(t_pad, n_heads_q, tensors["q"].shape[2], dtype=torch.bfloat16,
                                device=dev)
         self.logits = torch.empty(total, dtype=torch.float32, device=dev)
-        # Probabilities and argmax in one buffer (float32 [total] then int32 [n]).
-        self.d_res = torch.empty(total + n, dtype=torch.float32, device=dev)
-        self.probs, self.argmax = self.d_res[:total], self.d_res[total:].view(torch.int32)
+        # Probabilities and argmax in one pinned host buffer (float32 [total] then int32 [n])
+        # that the readout kernels write directly: no copy back.
         self.h_res = torch.empty(total + n, dtype=torch.float32, pin_memory=True)
         self.h_probs, self.h_argmax = self.h_res[:total], self.h_res[total:].view(torch.int32)
 
         # Argument lists checked once; every step reuses them.
         lib = load_library()
+        self._copy_fn = _hip_memcpy_async()
+        stream_handle = ctypes.c_void_p(self.stream.cuda_stream)
+        self._up_args = (ctypes.c_void_p(self.d_tab.data_ptr()),
+                         ctypes.c_void_p(self.h_tab.data_ptr()),
+                         ctypes.c_size_t(self.h_tab.numel() * 8), _HIP_MEMCPY_H2D, stream_handle)
         self._pack_fn = lib.blink_pack_ragged
         self._pack_args = pack_ragged_args(
             self.tail_len, self.prefix_len, self.token_budget, self.max_rows, self._order,
@@ -118,7 +143,7 @@ class ScoringStep:
         self._read_fn = lib.blink_label_readout
         self._read_args = label_readout(
             t["hidden"], self.d_last_row, t["w_u"], self.cand_ids, self.cand_off,
-            self.temperature, self.max_options, self.logits, self.probs, self.argmax,
+            self.temperature, self.max_options, self.logits, self.h_probs, self.h_argmax,
             stream=self.stream.cuda_stream, launch=False)
 
     @staticmethod
@@ -127,14 +152,20 @@ class ScoringStep:
         if rc != 0:
             raise BlinkError(rc, load_library().blink_last_error().decode("utf-8", "replace"))
 
+    def _copy(self, args):
+        if args[2].value == 0:
+            return
+        rc = self._copy_fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed with HIP error {rc}")
+
     def pack_and_upload(self) -> int:
         """Packs the tails into the pinned tables and queues their upload (one copy);
         returns the number of real tail tokens."""
         self._call(self._pack_fn, self._pack_args)
         if self._tp.value != self.pack.total_padded_tokens:
             raise BlinkError(BLINK_E_INVALID, "tensors were not laid out for this pack")
-        with self.torch.cuda.stream(self.stream):
-            self.d_tab.copy_(self.h_tab, non_blocking=True)
+        self._copy(self._up_args)
         return self._tv.value
 
     def attention(self, total_valid: int):
@@ -142,21 +173,17 @@ class ScoringStep:
         self._call(self._attn_fn, self._attn_args)
 
     def readout(self):
+        """Queues the readout; it writes probabilities and argmax into pinned host memory,
+        valid once the stream has been synchronised."""
         self._call(self._read_fn, self._read_args)
 
-    def download(self):
-        """Queues the copy of probabilities and argmax to pinned host memory."""
-        with self.torch.cuda.stream(self.stream):
-            self.h_res.copy_(self.d_res, non_blocking=True)
-
     def run(self, fetch: bool = True):
-        """One step. With ``fetch`` the probabilities and argmax are copied to pinned host
-        memory and the stream is synchronised; returns (probs, argmax) host arrays."""
+        """One step. With ``fetch`` the stream is synchronised and the (probs, argmax) host
+        arrays are returned; without it the step is only queued."""
         total_valid = self.pack_and_upload()
         self.attention(total_valid)
         self.readout()
         if not fetch:
             return None
-        self.download()
         self.stream.synchronize()
         return self.h_probs.numpy(), self.h_argmax.numpy()

@@ -1,0 +1,54 @@
+"""GPU parity of a whole scoring step (ScoringStep: host pack, table upload, attention, and the
+readout writing probabilities and argmax into pinned host memory) with the FP64 oracle.
+
+The step queues its work on the stream the caller picks, so it is checked both on torch's
+current stream and on a separate stream, and over several consecutive steps (buffers are
+reused, and the host result buffer is poisoned with NaN before each step)."""
+
+import numpy as np
+import pytest
+
+import synth
+from helpers import ATTN_TOL, PROB_TOL, Request, bf16_to_f32_host, check_argmax, device_bf16
+from helpers import valid_rows
+from oracle.attention import attention_full
+from oracle.readout import label_readout
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("side_stream", [False, True], ids=["current", "side"])
+def test_step_matches_oracle(side_stream):
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(1)
+    print(f"scoring step: config 1, side stream {side_stream}", flush=True)
+    req = Request(cfg)
+    ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
+    stream = torch.cuda.Stream() if side_stream else None
+    step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream)
+    h = req.tensors
+    ref = attention_full(h["q"], h["k_tail"], h["v_tail"], h.get("k_prefix"), h.get("v_prefix"),
+                         req.pack["token_offset"], req.tail_len, cfg.n_heads_q, cfg.n_heads_kv,
+                         cfg.scale)
+    z, p, a = label_readout(h["hidden"], req.pack["last_row"], h["w_u"], req.tables.cand_ids,
+                            req.tables.cand_off, cfg.temperature)
+    rows = valid_rows(req)
+    for it in range(3):
+        step.out.fill_(float("nan"))
+        step.h_res.fill_(float("nan"))
+        torch.cuda.synchronize()
+        probs, arg = step.run()
+        assert np.array_equal(step.h_token_offset, req.pack["token_offset"])
+        assert np.array_equal(step.h_last_row, req.pack["last_row"])
+        out = bf16_to_f32_host(step.out)
+        attn_err = float(np.abs(out[rows] - ref[rows]).max())
+        prob_err = float(np.abs(probs - p).max())
+        print(f"  step {it}: attention err {attn_err:.2e} probs err {prob_err:.2e}", flush=True)
+        assert attn_err <= ATTN_TOL
+        assert prob_err <= PROB_TOL
+        check_argmax(z, req.tables.cand_off, a, arg)
