@@ -121,11 +121,19 @@ struct Layout {
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tile must be whole KiB");
 };
 
+// The request's row tables, copied into LDS when the workgroup starts: every later lookup
+// (which question a row belongs to, where its tail starts) is then an LDS read, not a round
+// trip to memory on the way to the first tile.
+struct Tables {
+  int32_t start[BLINK_MAX_QUESTIONS + 1];  // valid_start: first real-token index of each question
+  int64_t toff[BLINK_MAX_QUESTIONS];       // token_offset: first packed row of each question
+};
+
 template <int D>
 struct Smem {
   __attribute__((aligned(16))) char k[kStages][Layout<D>::KBYTES];
   __attribute__((aligned(16))) char v[kStages][Layout<D>::VBYTES];
-  int32_t start[BLINK_MAX_QUESTIONS + 1];
+  Tables tab;
   int overflow;  // some row of the workgroup ended with a sum of probabilities above 2^kHeadroom
 };
 
@@ -147,6 +155,18 @@ __device__ inline int find_question(const int32_t *start, int n, int64_t c) {
 }
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint64_t u = uint64_t(x);
+  return int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(u))))) |
+                 (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(u >> 32))))) << 32));
+}
+
+// Workgroup barrier that orders LDS only: global stores issued before it are not waited for.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Pair reduction over lanes l and l ^ 32 (they hold the same query, different keys).
 __device__ inline float pair_max(float x) {
@@ -443,15 +463,15 @@ struct Unit {
   int qa, qz, posz;  // questions touched by the workgroup; last row's position in qz
 };
 
-__device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const Unit &u, int q) {
+__device__ inline TileSrc tail_from(const Args &a, const Tables &tab, const Unit &u, int q) {
   TileSrc s{};
   s.valid = false;
   for (; q <= u.qz; ++q) {
-    const int nq = uniform(start[q + 1] - start[q]);
+    const int nq = uniform(tab.start[q + 1] - tab.start[q]);
     const int limit = (q == u.qz) ? u.posz + 1 : nq;
     // A malformed table cannot make the loop run past the context length.
     if (limit > 0 && limit <= nq && nq <= BLINK_MAX_INPUT_TOKENS) {
-      s.rowbase = a.token_offset[q];
+      s.rowbase = uniform64(tab.toff[q]);
       s.kstart = 0;
       s.klimit = limit;
       s.q = q;
@@ -462,7 +482,7 @@ __device__ inline TileSrc tail_from(const Args &a, const int32_t *start, const U
   return s;
 }
 
-__device__ inline TileSrc first_tile(const Args &a, const int32_t *start, const Unit &u) {
+__device__ inline TileSrc first_tile(const Args &a, const Tables &tab, const Unit &u) {
   if (a.prefix_len > 0) {
     TileSrc s{};
     s.rowbase = 0;
@@ -472,15 +492,15 @@ __device__ inline TileSrc first_tile(const Args &a, const int32_t *start, const 
     s.valid = true;
     return s;
   }
-  return tail_from(a, start, u, u.qa);
+  return tail_from(a, tab, u, u.qa);
 }
 
-__device__ inline TileSrc next_tile(const Args &a, const int32_t *start, const Unit &u,
+__device__ inline TileSrc next_tile(const Args &a, const Tables &tab, const Unit &u,
                                     TileSrc s) {
   if (!s.valid) return s;
   s.kstart += kTileKeys;
   if (s.kstart < s.klimit) return s;
-  return tail_from(a, start, u, s.q < 0 ? u.qa : s.q + 1);
+  return tail_from(a, tab, u, s.q < 0 ? u.qa : s.q + 1);
 }
 
 struct RowTables {
@@ -510,7 +530,7 @@ __device__ inline void start_tiles(const Args &a, Smem<D> &sm, const Unit &u, in
                                    const TileSrc &first, int wave, const LoadPlan<D> &plan) {
   __builtin_amdgcn_sched_barrier(0);
   load_tile_async<D>(tile_rsrc<D>(a, g, first), sm.k[0], sm.v[0], wave, plan);
-  load_tile_async<D>(tile_rsrc<D>(a, g, next_tile(a, sm.start, u, first)), sm.k[1], sm.v[1],
+  load_tile_async<D>(tile_rsrc<D>(a, g, next_tile(a, sm.tab, u, first)), sm.k[1], sm.v[1],
                      wave, plan);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -529,11 +549,11 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   // the end of each pair makes the next pair visible and frees this one's stages.
   static_assert(kStages == 4, "pairs of tiles in a 4-stage ring");
   TileSrc cur = first;
-  TileSrc nxt = next_tile(a, sm.start, u, cur);  // tile t + 1
+  TileSrc nxt = next_tile(a, sm.tab, u, cur);  // tile t + 1
   if (!started) start_tiles<D>(a, sm, u, g, first, wave, plan);
   wait_tile_loads();
   __syncthreads();
-  TileSrc nxt2 = next_tile(a, sm.start, u, nxt);  // tile t + 2: the next pair's first
+  TileSrc nxt2 = next_tile(a, sm.tab, u, nxt);  // tile t + 2: the next pair's first
   int stage = 0;
   while (true) {
     // Tile t + 2 goes into the stage of tile t - 2 (the previous pair, done before the barrier).
@@ -595,7 +615,7 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     if (!nxt.valid) break;
     cur = nxt;
     nxt = nxt2;
-    nxt2 = next_tile(a, sm.start, u, nxt2);
+    nxt2 = next_tile(a, sm.tab, u, nxt2);
     stage = (stage + 1) & 3;
   }
   // The last loads (zeros for tiles past the end) must land before the stages are reused.
@@ -643,10 +663,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const int g = int(blockIdx.x % unsigned(a.hkv));
   const int64_t unit = blockIdx.x / unsigned(a.hkv);
 
-  for (int i = tid; i <= a.n; i += kThreads) sm.start[i] = a.valid_start[i];
+  for (int i = tid; i <= a.n; i += kThreads) {
+    sm.tab.start[i] = a.valid_start[i];
+    if (i < a.n) sm.tab.toff[i] = a.token_offset[i];
+  }
   if (tid == 0) sm.overflow = 0;
   __syncthreads();
-  const int64_t valid_total = min(int64_t(uniform(sm.start[a.n])), a.total_valid);
+  const int64_t valid_total = min(int64_t(uniform(sm.tab.start[a.n])), a.total_valid);
   const int64_t R = valid_total * G;
   const int64_t row0 = unit < a.full_units
                            ? unit * kRowsPerUnit
@@ -659,23 +682,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   Unit u;
   {
     const int64_t c0 = row0 / G, cz = (row_end - 1) / G;
-    u.qa = uniform(find_question(sm.start, a.n, c0));
-    u.qz = uniform(find_question(sm.start, a.n, cz));
-    u.posz = uniform(int(cz - sm.start[u.qz]));
+    u.qa = uniform(find_question(sm.tab.start, a.n, c0));
+    u.qz = uniform(find_question(sm.tab.start, a.n, cz));
+    u.posz = uniform(int(cz - sm.tab.start[u.qz]));
   }
   const int64_t wr0 = row0 + wave * kRowsPerWave;
   const bool wave_active = wr0 < row_end;
   int wqa = 0, wqz = -1, wposz = -1;
   if (wave_active) {
     const int64_t c0 = wr0 / G, cz = (min(wr0 + kRowsPerWave, row_end) - 1) / G;
-    wqa = uniform(find_question(sm.start, a.n, c0));
-    wqz = uniform(find_question(sm.start, a.n, cz));
-    wposz = uniform(int(cz - sm.start[wqz]));
+    wqa = uniform(find_question(sm.tab.start, a.n, c0));
+    wqz = uniform(find_question(sm.tab.start, a.n, cz));
+    wposz = uniform(int(cz - sm.tab.start[wqz]));
   }
 
   // The ring's first pair of K/V tiles goes out before the query rows are fetched, so the
   // two latencies overlap.
-  const TileSrc first = first_tile(a, sm.start, u);
+  const TileSrc first = first_tile(a, sm.tab, u);
   if (!first.valid) return;  // uniform: nothing visible (cannot happen for a valid table)
   const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
   start_tiles<D>(a, sm, u, g, first, wave, plan);
@@ -691,11 +714,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     rvalid[qb] = r < row_end;
     const int64_t c = rvalid[qb] ? r / G : 0;
     const int hl = int(r % G);
-    const int q = find_question(sm.start, a.n, c);
-    const int nq = sm.start[q + 1] - sm.start[q];
-    const int pos = int(c - sm.start[q]);
+    const int q = find_question(sm.tab.start, a.n, c);
+    const int nq = sm.tab.start[q + 1] - sm.tab.start[q];
+    const int pos = int(c - sm.tab.start[q]);
     rvalid[qb] = rvalid[qb] && pos >= 0 && pos < nq;
-    const int64_t tok = a.token_offset[q] + pos;
+    const int64_t tok = sm.tab.toff[q] + pos;
     rvalid[qb] = rvalid[qb] && tok >= 0 && tok < a.t_pad;
     rq[qb] = rvalid[qb] ? q : -1;
     rpos[qb] = pos;
@@ -731,8 +754,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   for (int qb = 0; qb < kQB; ++qb) over |= rvalid[qb] && !(pair_sum(rs[qb].l) <= kSumLimit);
   store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
   // Did any wave of the workgroup overflow? (The flag was cleared before the first barrier.)
+  // The barrier orders only the flag in LDS, so the workgroup does not wait for its stores to
+  // complete: it ends, and the next one starts on this CU, while they drain.
   if (__builtin_amdgcn_ballot_w64(over)) sm.overflow = 1;
-  __syncthreads();
+  lds_barrier();
   if (sm.overflow) {
     // Extreme inputs only: exact row maxima first, then the normal pass with those references;
     // its rows overwrite the ones just stored. (The accumulators are reused: the stored values
