@@ -623,17 +623,36 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   __syncthreads();
 }
 
-// Normalise and store bf16 rows (four consecutive dims per 8-byte store).
+// A wave's output rows staged in LDS: bf16 rows padded to RS bytes, then each row's
+// destination (element offset into out, or -1 for a row that is not stored).
 template <int D>
-__device__ inline void store_rows(const Args &a, const f32x16 (&o)[kQB][D / 32],
+struct OutStage {
+  static constexpr int RS = D * 2 + 16;
+  static constexpr int BYTES = kRowsPerWave * RS + kRowsPerWave * 8;
+  static_assert(RS % 16 == 0 && BYTES % 16 == 0, "16-byte LDS reads");
+  static_assert(kWaves * BYTES <= kStages * (Layout<D>::KBYTES + Layout<D>::VBYTES),
+                "every wave's rows fit in the K/V ring");
+};
+
+// Normalise the wave's rows to bf16 and store them. In the accumulator layout a lane holds
+// 8-byte pieces of one row, so storing from registers makes every instruction write 16 bytes
+// into each of 32 rows. The rows go through LDS instead (`stage`, this wave's part of the K/V
+// ring, free once the tiles are done), so that each global store writes 64 x 16 contiguous
+// bytes: whole rows, whole cache lines.
+template <int D>
+__device__ inline void store_rows(const Args &a, char *stage, const f32x16 (&o)[kQB][D / 32],
                                   const RowState (&rs)[kQB], const bool (&rvalid)[kQB],
-                                  const int64_t (&rtok)[kQB], const int (&rhead)[kQB], int half) {
+                                  const int64_t (&rtok)[kQB], const int (&rhead)[kQB],
+                                  int lane) {
+  using S = OutStage<D>;
+  const int col = lane & 31, half = lane >> 5;
+  int64_t *dst = reinterpret_cast<int64_t *>(stage + kRowsPerWave * S::RS);
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const float l = pair_sum(rs[qb].l);
-    if (!rvalid[qb]) continue;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    uint16_t *orow = a.out + (rtok[qb] * a.hq + rhead[qb]) * D + 4 * half;
+    const int row = 32 * qb + col;
+    char *lrow = stage + row * S::RS + 8 * half;  // dims 4 * half + 8 * grp + 32 * db
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -646,9 +665,21 @@ __device__ inline void store_rows(const Args &a, const f32x16 (&o)[kQB][D / 32],
           packed[j] = uint32_t(__builtin_bit_cast(uint16_t, x0)) |
                       (uint32_t(__builtin_bit_cast(uint16_t, x1)) << 16);
         }
-        *reinterpret_cast<u32x2 *>(orow + db * 32 + 8 * grp) = packed;
+        *reinterpret_cast<u32x2 *>(lrow + (db * 32 + 8 * grp) * 2) = packed;
       }
     }
+    if (half == 0) dst[row] = rvalid[qb] ? (rtok[qb] * a.hq + rhead[qb]) * D : int64_t(-1);
+  }
+  // Lanes read what other lanes of the same wave wrote: one wave's LDS operations complete in
+  // order, so only the compiler has to keep them in order.
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  constexpr int kChunks = D * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave * kChunks / 64; ++i) {
+    const int k = lane + 64 * i, row = k / kChunks, chunk = k % kChunks;
+    const int64_t d = dst[row];
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * S::RS + chunk * 16);
+    if (d >= 0) *reinterpret_cast<u32x4 *>(a.out + d + chunk * 8) = v;
   }
 }
 
@@ -742,6 +773,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const int vlane = v_lane_offset<D>(lane);
 
   const RowTables rt{rq, rpos};
+  // This wave's part of the K/V ring for staging its output rows (used after the tiles).
+  static_assert(offsetof(Smem<D>, v) == offsetof(Smem<D>, k) + sizeof(sm.k),
+                "the K and V stages form one contiguous ring");
+  char *ostage = &sm.k[0][0] + wave * OutStage<D>::BYTES;
   const WaveSpan ws{wave_active, wqa, wqz, wposz};
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
@@ -752,7 +787,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   bool over = false;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) over |= rvalid[qb] && !(pair_sum(rs[qb].l) <= kSumLimit);
-  store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
+  store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
   // Did any wave of the workgroup overflow? (The flag was cleared before the first barrier.)
   // The barrier orders only the flag in LDS, so the workgroup does not wait for its stores to
   // complete: it ends, and the next one starts on this CU, while they drain.
@@ -768,7 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     init_rows<D>(o, rs, false);
     run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
                  false);
-    store_rows<D>(a, o, rs, rvalid, rtok, rhead, half);
+    store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
   }
 #endif
 }
