@@ -203,9 +203,10 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_ms = float(np.mean([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]))
-    read_ms = float(np.mean([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]))
+    attn_each = np.array([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)])
+    read_each = np.array([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)])
     ev.close()
+    attn_ms, read_ms = float(attn_each.mean()), float(read_each.mean())
     flops = attention_flops(cfg, tables.tail_len)
     abytes = attention_bytes(cfg, tables.tail_len)
     rbytes = readout_bytes(cfg, tables.cand_ids, cfg.n_questions)
@@ -262,6 +263,12 @@ def main():
             "readout_gbps": rbytes / (read_ms * 1e-3) / 1e9,
             "readout_hbm_frac": rbytes / (read_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "readout_algorithmic_bytes": rbytes,
+            # Spread over the timed steps (median, 10th and 90th percentile, ms).
+            "attention_ms_p50_p10_p90": [float(np.percentile(attn_each, q)) for q in (50, 10, 90)],
+            "readout_ms_p50_p10_p90": [float(np.percentile(read_each, q)) for q in (50, 10, 90)],
+            # Questions per second of GPU kernel time alone (attention + readout), without the
+            # host pack, the table upload and the synchronisation that `value` includes.
+            "kernel_only_questions_per_s": n / ((attn_ms + read_ms) * 1e-3),
         },
         "cpu_baseline": baseline,
     }
