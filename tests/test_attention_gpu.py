@@ -72,6 +72,35 @@ def test_full_size_sampled(number):
     assert np.isfinite(got[valid_rows(req)]).all()
 
 
+# The largest context the boundary accepts (prefix + tail = 131072 tokens): one question whose
+# tail is the whole context with no prefix (2048 tiles of causal tail attention, as when the
+# prefix itself is encoded), and the longest prefix with a one-token tail.
+MAXIMUM = {
+    "tail_131072_no_prefix": synth.config(4, n_questions=1, tail_lo=131072, tail_hi=131072),
+    "prefix_131071_tail_1": synth.config(2, prefix_len=131071, n_questions=1, tail_lo=1,
+                                         tail_hi=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MAXIMUM))
+def test_maximum_context_sampled(name):
+    cfg = MAXIMUM[name]
+    print(f"attention at the maximum context: {name}", flush=True)
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    got = run_attention(req)
+    samples = sample_rows(req, 24, seed=11)
+    ts = req.tensors
+    ref = attention_rows(ts["q"], ts["k_tail"], ts["v_tail"], ts.get("k_prefix"),
+                         ts.get("v_prefix"), req.pack["token_offset"], req.tail_len,
+                         cfg.n_heads_q, cfg.n_heads_kv, cfg.scale, samples)
+    off = req.pack["token_offset"]
+    picked = np.stack([got[off[i] + t, h] for i, t, h in samples])
+    err = np.abs(picked - ref).max()
+    print(f"  max abs err {err:.3e} over {len(samples)} sampled rows", flush=True)
+    assert np.isfinite(picked).all() and err <= ATTN_TOL
+    assert np.isfinite(got[valid_rows(req)]).all()
+
+
 def test_padding_content_is_never_read():
     cfg = SMALL["4b_like_small"]
     req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
