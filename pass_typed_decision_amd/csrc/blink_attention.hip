@@ -623,22 +623,33 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
   __syncthreads();
 }
 
-// A wave's output rows staged in LDS: bf16 rows padded to RS bytes, then each row's
-// destination (element offset into out, or -1 for a row that is not stored).
+// A wave's output rows staged in LDS, half a row (D / 2 dims) at a time: bf16 half rows
+// padded to RS bytes, then each row's destination (element offset into out, or -1 for a row
+// that is not stored). The waves' areas fill two stages of the ring: the K halves of the pair
+// first, then its V halves.
 template <int D>
 struct OutStage {
-  static constexpr int RS = D * 2 + 16;
+  static constexpr int RS = D + 16;
   static constexpr int BYTES = kRowsPerWave * RS + kRowsPerWave * 8;
+  static constexpr int IN_K = 2 * Layout<D>::KBYTES / BYTES;  // areas in the pair's K stages
   static_assert(RS % 16 == 0 && BYTES % 16 == 0, "16-byte LDS reads");
-  static_assert(kWaves * BYTES <= kStages * (Layout<D>::KBYTES + Layout<D>::VBYTES),
-                "every wave's rows fit in the K/V ring");
+  static_assert(IN_K + 2 * Layout<D>::VBYTES / BYTES >= kWaves,
+                "every wave's half rows fit in two stages of the K/V ring");
 };
+
+// This wave's staging area in the stage pair (pair, pair + 1), pair = 0 or 2.
+template <int D>
+__device__ inline char *out_stage(Smem<D> &sm, int pair, int wave) {
+  using S = OutStage<D>;
+  return wave < S::IN_K ? &sm.k[pair][0] + wave * S::BYTES
+                        : &sm.v[pair][0] + (wave - S::IN_K) * S::BYTES;
+}
 
 // Normalise the wave's rows to bf16 and store them. In the accumulator layout a lane holds
 // 8-byte pieces of one row, so storing from registers makes every instruction write 16 bytes
-// into each of 32 rows. The rows go through LDS instead (`stage`, this wave's part of the K/V
-// ring, free once the tiles are done), so that each global store writes 64 x 16 contiguous
-// bytes: whole rows, whole cache lines.
+// into each of 32 rows. The rows go through LDS instead (`stage`, this wave's area in two idle
+// stages of the K/V ring), half a row at a time, so that each global store writes 64 x 16
+// bytes of whole 128-byte lines: eight half rows of 128 bytes (D = 128).
 template <int D>
 __device__ inline void store_rows(const Args &a, char *stage, const f32x16 (&o)[kQB][D / 32],
                                   const RowState (&rs)[kQB], const bool (&rvalid)[kQB],
@@ -647,39 +658,47 @@ __device__ inline void store_rows(const Args &a, char *stage, const f32x16 (&o)[
   using S = OutStage<D>;
   const int col = lane & 31, half = lane >> 5;
   int64_t *dst = reinterpret_cast<int64_t *>(stage + kRowsPerWave * S::RS);
+  float inv[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const float l = pair_sum(rs[qb].l);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int row = 32 * qb + col;
-    char *lrow = stage + row * S::RS + 8 * half;  // dims 4 * half + 8 * grp + 32 * db
+    inv[qb] = l > 0.f ? 1.0f / l : 0.f;
+    if (half == 0)
+      dst[32 * qb + col] = rvalid[qb] ? (rtok[qb] * a.hq + rhead[qb]) * D : int64_t(-1);
+  }
+  constexpr int kChunks = D / 16;  // 16-byte chunks per half row
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+  for (int part = 0; part < 2; ++part) {  // dims [part * D / 2, (part + 1) * D / 2)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        u32x2 packed;
+    for (int qb = 0; qb < kQB; ++qb) {
+      char *lrow = stage + (32 * qb + col) * S::RS + 8 * half;  // dims 4 * half + 8 * grp + 32 * db
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const __bf16 x0 = (__bf16)(o[qb][db][4 * grp + 2 * j] * inv);
-          const __bf16 x1 = (__bf16)(o[qb][db][4 * grp + 2 * j + 1] * inv);
-          packed[j] = uint32_t(__builtin_bit_cast(uint16_t, x0)) |
-                      (uint32_t(__builtin_bit_cast(uint16_t, x1)) << 16);
+      for (int db = part * D / 64; db < (part + 1) * D / 64; ++db) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          u32x2 packed;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const __bf16 x0 = (__bf16)(o[qb][db][4 * grp + 2 * j] * inv[qb]);
+            const __bf16 x1 = (__bf16)(o[qb][db][4 * grp + 2 * j + 1] * inv[qb]);
+            packed[j] = uint32_t(__builtin_bit_cast(uint16_t, x0)) |
+                        (uint32_t(__builtin_bit_cast(uint16_t, x1)) << 16);
+          }
+          *reinterpret_cast<u32x2 *>(lrow + ((db - part * D / 64) * 32 + 8 * grp) * 2) = packed;
         }
-        *reinterpret_cast<u32x2 *>(lrow + (db * 32 + 8 * grp) * 2) = packed;
       }
     }
-    if (half == 0) dst[row] = rvalid[qb] ? (rtok[qb] * a.hq + rhead[qb]) * D : int64_t(-1);
-  }
-  // Lanes read what other lanes of the same wave wrote: one wave's LDS operations complete in
-  // order, so only the compiler has to keep them in order.
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  constexpr int kChunks = D * 2 / 16;  // 16-byte chunks per row
+    // Lanes read what other lanes of the same wave wrote (and then overwrite what they read):
+    // one wave's LDS operations complete in order, so only the compiler has to keep them so.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave * kChunks / 64; ++i) {
-    const int k = lane + 64 * i, row = k / kChunks, chunk = k % kChunks;
-    const int64_t d = dst[row];
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * S::RS + chunk * 16);
-    if (d >= 0) *reinterpret_cast<u32x4 *>(a.out + d + chunk * 8) = v;
+    for (int i = 0; i < kRowsPerWave * kChunks / 64; ++i) {
+      const int k = lane + 64 * i, row = k / kChunks, chunk = k % kChunks;
+      const int64_t d = dst[row];
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * S::RS + chunk * 16);
+      if (d >= 0) *reinterpret_cast<u32x4 *>(a.out + d + part * D / 2 + chunk * 8) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 }
 
@@ -773,10 +792,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const int vlane = v_lane_offset<D>(lane);
 
   const RowTables rt{rq, rpos};
-  // This wave's part of the K/V ring for staging its output rows (used after the tiles).
-  static_assert(offsetof(Smem<D>, v) == offsetof(Smem<D>, k) + sizeof(sm.k),
-                "the K and V stages form one contiguous ring");
-  char *ostage = &sm.k[0][0] + wave * OutStage<D>::BYTES;
+  // This wave's area in stages 0 and 1 for staging its output rows (used after the tiles).
+  char *ostage = out_stage<D>(sm, 0, wave);
   const WaveSpan ws{wave_active, wqa, wqz, wposz};
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
