@@ -35,7 +35,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
 # counted on; a changed kernel reports null until it is counted again.
 MEASURED_TRAFFIC = {
-    2: ("81b7fdc5c6cd6beb85e6eb6640f57edf62c73e0577de08c7d6f7352171687ff4", 129673760),
+    2: ("0a13b5abe1b7cb8d6e8cc8f4d5f6e91b2f8a87cc7e2c2cba5ee81987165fcdda", 129673760),
 }
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 

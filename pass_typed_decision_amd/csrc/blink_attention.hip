@@ -49,9 +49,21 @@
 //    on which other rows share its wave.
 //  * Prefix tiles first (unmasked except the last partial tile), then the tail tiles of each
 //    question the unit touches, masked per lane (same question and key <= position).
+//  * Two tile paths. Whole prefix tiles for a wave whose rows all have their reference take a
+//    branch-free path with no row maxima: both 32-key score blocks, then exp2, bf16, row sums
+//    and PV, with the next tiles' loads issued between the score MFMAs, which run at raised
+//    wave priority so the matrix pipe is fed ahead of other waves' softmax. Everything else
+//    (masked tail tiles, the last partial prefix tile, a row's first tile) takes the general
+//    path, one 32-key block at a time.
+//  * The request's row tables (valid_start, token_offset) are copied into LDS when the
+//    workgroup starts, so every lookup on the way to the first tile is an LDS read.
+//  * Output rows go through LDS (two idle stages of the ring, half a row at a time) so that
+//    every global store writes 64 x 16 contiguous bytes of whole cache lines; from registers, a
+//    store instruction would write 16 bytes into each of 32 rows.
 //  * blockIdx -> (KV head, unit) puts the KV head in the low bits, so with 8 KV heads each of
 //    the 8 XCDs (dispatch is round-robin over XCDs) streams one head's prefix K/V through its
-//    own L2.
+//    own L2. The rows left for the last round of workgroups are re-cut into smaller units
+//    (unit_split) so that that round covers every CU.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
