@@ -708,7 +708,12 @@ __device__ inline void store_rows(const Args &a, char *stage, const f32x16 (&o)[
       const int k = lane + 64 * i, row = k / kChunks, chunk = k % kChunks;
       const int64_t d = dst[row];
       const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * S::RS + chunk * 16);
-      if (d >= 0) *reinterpret_cast<u32x4 *>(a.out + d + part * D / 2 + chunk * 8) = v;
+      // Non-temporal: the kernel never reads its output back, and streaming it past the
+      // caches leaves them clean for whatever runs next (the readout after a large request
+      // otherwise starts by writing back hundreds of MB of dirty lines).
+      if (d >= 0)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(a.out + d + part * D / 2 +
+                                                                 chunk * 8));
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
