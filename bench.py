@@ -35,7 +35,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
 # counted on; a changed kernel reports null until it is counted again.
 MEASURED_TRAFFIC = {
-    2: ("0a13b5abe1b7cb8d6e8cc8f4d5f6e91b2f8a87cc7e2c2cba5ee81987165fcdda", 129673760),
+    2: ("bd713bd1efb5c2796b23cdf16b24a453c01c704b15c75cb5bc97e5b0b0cfa8b9", 126240832),
 }
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 
