@@ -14,7 +14,8 @@ It follows the blink.py page (thegovind/blink-4b):
                      PREFIX_CACHE comment in "constants the deployment sets");
   * ``readout``   -- last-valid-row gather, FP64 dot against the offered labels' unembedding
                      rows, temperature softmax and first-index argmax ("torch engine" section:
-                     _read; "answer assembly" section: softmax and answer_for).
+                     _read; "answer assembly" section: softmax and answer_for), and its
+                     batched form over the distinct label rows (_read_batched).
 
 Arithmetic is float64 throughout; bf16 inputs are widened exactly.
 Every function is pinned by tests under ``tests/test_oracle_*.py``; none is "parity unpinned".
@@ -27,7 +28,7 @@ from .attention import (
     attention_decomposed,
     attention_rows,
 )
-from .readout import label_readout, softmax_t, MAX_OPTIONS
+from .readout import label_readout, label_readout_batched, label_rows, softmax_t, MAX_OPTIONS
 from .path import score_request
 
 __all__ = [
@@ -41,6 +42,8 @@ __all__ = [
     "attention_decomposed",
     "attention_rows",
     "label_readout",
+    "label_readout_batched",
+    "label_rows",
     "softmax_t",
     "score_request",
 ]
