@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--readout", default="per_option", choices=("per_option", "batched"),
+                    help="readout form: per option (default), or batched over the distinct "
+                         "label rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (the known-size "
                          "reference for hardware byte counters) and exit after it")
@@ -183,7 +186,17 @@ def main():
     stream = torch.cuda.current_stream()
     step = blink.ScoringStep(tables.tail_len, tables.cand_ids, tables.cand_off, tensors,
                              cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
-                             cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream)
+                             cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream,
+                             readout=args.readout)
+    label_pack_ms = None
+    if step.readout_form == "batched":
+        # The distinct-row table is built once per request, with the option table's upload;
+        # its host cost is reported beside the step, not inside it.
+        reps = 20
+        t_lp = time.perf_counter()
+        for _ in range(reps):
+            blink.pack_labels(tables.cand_ids, tables.cand_off, cfg.vocab)
+        label_pack_ms = (time.perf_counter() - t_lp) * 1e3 / reps
 
     for _ in range(args.warmup):
         step.run()
@@ -269,6 +282,9 @@ def main():
             # Questions per second of GPU kernel time alone (attention + readout), without the
             # host pack, the table upload and the synchronisation that `value` includes.
             "kernel_only_questions_per_s": n / ((attn_ms + read_ms) * 1e-3),
+            "readout_form": step.readout_form,
+            "label_rows": (None if step.label_rows is None else int(step.label_rows.n_rows)),
+            "label_pack_host_ms_once_per_request": label_pack_ms,
         },
         "cpu_baseline": baseline,
     }

@@ -55,7 +55,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 1
+#define BLINK_ABI_VERSION 2
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -96,6 +96,32 @@ int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, int32_t pref
                       int32_t *batch_first, int32_t *batch_width, int64_t *batch_base,
                       int32_t *n_batches, int64_t *total_padded_tokens,
                       int64_t *total_valid_tokens);
+
+/*
+ * blink_pack_labels -- host, synchronous, integer only.
+ *
+ * Distinct label rows of an option table ("torch engine" section, _read_batched: the
+ * distinct label token ids of the questions, in ascending order, each gathered once). The
+ * flat option entries are the positions 0..total-1 of cand_ids (total = cand_off[n]).
+ *
+ * Inputs (host):
+ *   cand_ids[total]   token id of each offered label, each in [0, vocab) (else
+ *                     BLINK_E_INVALID, naming the entry)
+ *   cand_off[n+1]     CSR offsets: cand_off[0] = 0, 1 <= K_i <= 255 (else BLINK_E_LIMIT,
+ *                     "K options per choice; supported 1-255")
+ *   n_questions       1..512 (else BLINK_E_LIMIT)
+ *   vocab             1..2^31
+ * Outputs (host arrays the caller allocates for the worst case, U = total):
+ *   row_id[U]         the distinct ids, strictly ascending; the first *n_rows are written
+ *   row_first[U+1]    the entries with id row_id[j] are row_entry[row_first[j] ..
+ *                     row_first[j+1]); row_first[*n_rows] = total
+ *   row_entry[total]  flat entry indices grouped by row, ascending within each row
+ *   n_rows            number of distinct ids
+ * Ids that repeat inside one question are allowed here (the readout's callers refuse them).
+ */
+int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_off, int32_t n_questions,
+                      int64_t vocab, int32_t *row_id, int32_t *row_first, int32_t *row_entry,
+                      int32_t *n_rows);
 
 /*
  * blink_prefix_tail_attention -- device, asynchronous.
@@ -166,6 +192,36 @@ int blink_label_readout(const void *hidden, int64_t hidden_rows, int32_t d_model
                         int32_t n_questions, int64_t total_candidates, int32_t max_options,
                         float temperature, float *d_logits, float *d_probs,
                         int32_t *d_argmax, void *stream);
+
+/*
+ * blink_label_readout_batched -- device, asynchronous.
+ *
+ * The same readout as blink_label_readout in its batched form ("torch engine" section,
+ * _read_batched): each distinct label row of the request is read from memory once and
+ * scored against the hidden row of every question that offers it, instead of once per
+ * offering question. Outputs, their meaning and the error behaviour are those of
+ * blink_label_readout, and every logit is the same FP32 dot product accumulated in the same
+ * order, so the results are bitwise those of blink_label_readout.
+ *
+ *   hidden, d_last_row, w_u, vocab, d_model, d_cand_off, n_questions, total_candidates,
+ *   max_options, temperature, d_logits, d_probs, d_argmax: as in blink_label_readout
+ *   d_row_id     int32 [n_rows]   device: distinct ids (blink_pack_labels row_id)
+ *   d_row_first  int32 [n_rows+1] device: CSR offsets into d_row_entry (row_first)
+ *   d_row_entry  int32 [total_candidates] device: flat entries grouped by row (row_entry)
+ *   n_rows       1..total_candidates
+ * The three row tables must be blink_pack_labels' output for the same option table; for
+ * other contents every access still stays inside the sizes passed in, an out-of-range id
+ * gives NaN logits for its entries, and entries no row lists are left with unspecified
+ * results.
+ */
+int blink_label_readout_batched(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                                const int64_t *d_last_row, const void *w_u, int64_t vocab,
+                                const int32_t *d_cand_off, int32_t n_questions,
+                                int64_t total_candidates, int32_t max_options,
+                                const int32_t *d_row_id, const int32_t *d_row_first,
+                                const int32_t *d_row_entry, int32_t n_rows, float temperature,
+                                float *d_logits, float *d_probs, int32_t *d_argmax,
+                                void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,10 +23,13 @@ from ._binding import (
     MAX_OPTIONS,
     MAX_QUESTIONS,
     TOKEN_BUDGET,
+    LabelRows,
     Pack,
     check_candidate_table,
     label_readout,
+    label_readout_batched,
     load_library,
+    pack_labels,
     pack_ragged,
     prefix_tail_attention,
 )
@@ -44,10 +47,13 @@ __all__ = [
     "MAX_OPTIONS",
     "MAX_QUESTIONS",
     "TOKEN_BUDGET",
+    "LabelRows",
     "Pack",
     "check_candidate_table",
     "label_readout",
+    "label_readout_batched",
     "load_library",
+    "pack_labels",
     "pack_ragged",
     "prefix_tail_attention",
     "ScoringStep",

@@ -32,6 +32,8 @@ EXPORTS = (
     "blink_pack_ragged",
     "blink_prefix_tail_attention",
     "blink_label_readout",
+    "blink_pack_labels",
+    "blink_label_readout_batched",
 )
 
 
@@ -80,6 +82,13 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.blink_label_readout.restype = ctypes.c_int
     lib.blink_label_readout.argtypes = [
         _P, _I64, _I32, _P, _P, _I64, _P, _P, _I32, _I64, _I32, _F32, _P, _P, _P, _P,
+    ]
+    lib.blink_pack_labels.restype = ctypes.c_int
+    lib.blink_pack_labels.argtypes = [_PI32, _PI32, _I32, _I64, _PI32, _PI32, _PI32, _PI32]
+    lib.blink_label_readout_batched.restype = ctypes.c_int
+    lib.blink_label_readout_batched.argtypes = [
+        _P, _I64, _I32, _P, _P, _I64, _P, _I32, _I64, _I32, _P, _P, _P, _I32, _F32, _P, _P, _P,
+        _P,
     ]
     _lib = lib
     return lib
@@ -268,6 +277,75 @@ def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
     if not launch:
         return args
     _check(lib.blink_label_readout(*args))
+
+
+@dataclass
+class LabelRows:
+    """Result of blink_pack_labels (host arrays)."""
+
+    row_id: np.ndarray  # [n_rows] distinct label ids, ascending
+    row_first: np.ndarray  # [n_rows + 1]
+    row_entry: np.ndarray  # [total] flat option entries grouped by row
+    n_rows: int
+
+
+def pack_labels(cand_ids, cand_off, vocab: int) -> LabelRows:
+    """Distinct label rows of an option table (blink_pack_labels)."""
+    lib = load_library()
+    ids = np.ascontiguousarray(np.asarray(cand_ids, dtype=np.int32))
+    off = np.ascontiguousarray(np.asarray(cand_off, dtype=np.int32))
+    n = int(off.shape[0]) - 1
+    total = int(ids.shape[0])
+    if n < 0 or (n and int(off[-1]) != total):
+        raise BlinkError(BLINK_E_INVALID, "candidate offsets must run from 0 to len(cand_ids)")
+    cap = max(total, 1)
+    row_id = np.zeros(cap, np.int32)
+    row_first = np.zeros(cap + 1, np.int32)
+    row_entry = np.zeros(cap, np.int32)
+    u = ctypes.c_int32(0)
+    src_ids = ids if total else np.zeros(1, np.int32)
+    src_off = off if n >= 0 and off.shape[0] else np.zeros(1, np.int32)
+    _check(lib.blink_pack_labels(_ptr(src_ids, ctypes.c_int32), _ptr(src_off, ctypes.c_int32), n,
+                                 int(vocab), _ptr(row_id, ctypes.c_int32),
+                                 _ptr(row_first, ctypes.c_int32), _ptr(row_entry, ctypes.c_int32),
+                                 ctypes.byref(u)))
+    k = u.value
+    return LabelRows(row_id[:k], row_first[:k + 1], row_entry[:total], k)
+
+
+def label_readout_batched(hidden, last_row, w_u, cand_off, row_id, row_first, row_entry,
+                          temperature: float, max_options: int, logits, probs, argmax,
+                          stream=None, launch: bool = True):
+    """Launches blink_label_readout_batched: as label_readout, with the option table given
+    by its CSR offsets and its distinct-row tables (row_id int32 [U], row_first int32 [U + 1],
+    row_entry int32 [sum K], device; from pack_labels). With ``launch=False`` returns the
+    checked argument list instead, for repeated launches."""
+    import torch
+
+    bf = torch.bfloat16
+    if hidden.dim() != 2 or w_u.dim() != 2 or hidden.shape[1] != w_u.shape[1]:
+        raise BlinkError(BLINK_E_INVALID, "hidden and w_u must be 2-D with the same width")
+    n = int(last_row.shape[0])
+    total = int(row_entry.shape[0])
+    u = int(row_id.shape[0])
+    if int(cand_off.shape[0]) != n + 1:
+        raise BlinkError(BLINK_E_INVALID, "cand_off must have n + 1 entries")
+    if int(row_first.shape[0]) != u + 1:
+        raise BlinkError(BLINK_E_INVALID, "row_first must have n_rows + 1 entries")
+    if int(logits.shape[0]) != total or int(probs.shape[0]) != total or int(argmax.shape[0]) != n:
+        raise BlinkError(BLINK_E_INVALID, "output sizes do not match the candidate table")
+    lib = load_library()
+    args = [
+        _dev(hidden, bf, "hidden"), int(hidden.shape[0]), int(hidden.shape[1]),
+        _dev(last_row, torch.int64, "last_row"), _dev(w_u, bf, "w_u"), int(w_u.shape[0]),
+        _dev(cand_off, torch.int32, "cand_off"), n, total, int(max_options),
+        _dev(row_id, torch.int32, "row_id"), _dev(row_first, torch.int32, "row_first"),
+        _dev(row_entry, torch.int32, "row_entry"), u, float(temperature),
+        _dev(logits, torch.float32, "logits"), _dev_or_pinned(probs, torch.float32, "probs"),
+        _dev_or_pinned(argmax, torch.int32, "argmax"), _stream(stream)]
+    if not launch:
+        return args
+    _check(lib.blink_label_readout_batched(*args))
 
 
 def check_candidate_table(cand_ids, cand_off, vocab: int) -> int:

@@ -122,3 +122,67 @@ extern "C" int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, i
   *total_valid_tokens = running;
   return blink::ok();
 }
+
+// Distinct label rows of an option table (blink.py page, "torch engine" section,
+// _read_batched: the distinct label ids of the questions, ascending, each gathered once).
+// One bit per vocabulary id marks the ids in use; a scan of the bit words lists them in
+// ascending order and gives each id its column; a stable counting sort by column then
+// groups the flat option entries under their row, in ascending entry order.
+extern "C" int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_off,
+                                 int32_t n_questions, int64_t vocab, int32_t *row_id,
+                                 int32_t *row_first, int32_t *row_entry, int32_t *n_rows) {
+  using blink::fail;
+  if (!cand_ids || !cand_off || !row_id || !row_first || !row_entry || !n_rows)
+    return fail(BLINK_E_INVALID, "blink_pack_labels: a pointer argument is NULL");
+  if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
+    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
+  if (vocab < 1 || vocab > (int64_t(1) << 31))
+    return fail(BLINK_E_INVALID, "vocab %lld outside 1..2^31", (long long)vocab);
+  if (cand_off[0] != 0) return fail(BLINK_E_INVALID, "candidate offsets must start at 0");
+  for (int i = 0; i < n_questions; ++i) {
+    const int64_t k = int64_t(cand_off[i + 1]) - cand_off[i];
+    if (k < 1 || k > BLINK_MAX_OPTIONS)
+      return fail(BLINK_E_LIMIT, "%lld options per choice; supported 1-%d", (long long)k,
+                  BLINK_MAX_OPTIONS);
+  }
+  const int32_t total = cand_off[n_questions];
+  for (int32_t e = 0; e < total; ++e)
+    if (cand_ids[e] < 0 || cand_ids[e] >= vocab)
+      return fail(BLINK_E_INVALID, "option entry %d has token id %d outside [0, %lld)", e,
+                  cand_ids[e], (long long)vocab);
+
+  // Per-thread work arrays, reused across calls. Their addresses are taken once: inside a
+  // shared library every access to a thread_local goes through a TLS lookup call.
+  static thread_local std::vector<uint64_t> tl_bits;
+  static thread_local std::vector<int32_t> tl_word_base, tl_col, tl_cursor;
+  const size_t words = size_t((vocab + 63) >> 6);
+  tl_bits.assign(words, 0);
+  tl_word_base.resize(words);
+  tl_col.resize(size_t(total));
+  uint64_t *bits = tl_bits.data();
+  int32_t *word_base = tl_word_base.data();
+  int32_t *col = tl_col.data();
+  for (int32_t e = 0; e < total; ++e) {
+    const uint32_t t = uint32_t(cand_ids[e]);
+    bits[t >> 6] |= uint64_t(1) << (t & 63);
+  }
+  int32_t u = 0;
+  for (size_t w = 0; w < words; ++w) {
+    word_base[w] = u;
+    for (uint64_t m = bits[w]; m; m &= m - 1)
+      row_id[u++] = int32_t(w * 64 + size_t(__builtin_ctzll(m)));
+  }
+  tl_cursor.assign(size_t(u) + 1, 0);
+  int32_t *cursor = tl_cursor.data();
+  for (int32_t e = 0; e < total; ++e) {
+    const uint32_t t = uint32_t(cand_ids[e]);
+    const uint64_t below = bits[t >> 6] & ((uint64_t(1) << (t & 63)) - 1);
+    col[e] = word_base[t >> 6] + __builtin_popcountll(below);
+    ++cursor[col[e] + 1];
+  }
+  for (int32_t j = 0; j < u; ++j) cursor[j + 1] += cursor[j];
+  for (int32_t j = 0; j <= u; ++j) row_first[j] = cursor[j];
+  for (int32_t e = 0; e < total; ++e) row_entry[cursor[col[e]]++] = e;
+  *n_rows = u;
+  return blink::ok();
+}

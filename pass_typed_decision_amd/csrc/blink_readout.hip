@@ -20,6 +20,9 @@
 //    max, exp, sum, normalise, and the first index of the largest logit.
 // Small tables (launch-latency-bound) take one launch, label_readout_fused_kernel: one
 // workgroup per question scores its rows and finishes it in the same kernel.
+// The batched form (blink_label_readout_batched, after _read_batched) replaces the first
+// launch of the streaming path with label_logits_rows_kernel, which reads each distinct label
+// row once however many questions offer it.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -113,6 +116,65 @@ __global__ __launch_bounds__(64 * kFlatWaves) void label_logits_flat_kernel(
   }
   const float z = wave_sum(acc);
   if (lane == 0) logits[r] = (id_ok && h_ok) ? z : __builtin_nanf("");
+}
+
+// Batched form (blink.py page, "torch engine" section, _read_batched): every distinct label
+// row of the request is fetched from HBM once and scored against the hidden row of each
+// question that offers it. One wave per distinct row j: its unembedding row row_id[j] is
+// loaded once (a streaming load: nothing reads it again), then for every flat option entry
+// e in row_entry[row_first[j] .. row_first[j+1]) the owning question's hidden row (an L2 hit)
+// gives logits[e]. Blocks map to XCDs as in label_logits_flat_kernel.
+template <int NCH>
+__global__ __launch_bounds__(64 * kFlatWaves) void label_logits_rows_kernel(
+    const uint16_t *__restrict__ hidden, int64_t hidden_rows, int d_model,
+    const int64_t *__restrict__ last_row, const uint16_t *__restrict__ w_u, int64_t vocab,
+    const int32_t *__restrict__ cand_off, int n, int64_t total,
+    const int32_t *__restrict__ row_id, const int32_t *__restrict__ row_first,
+    const int32_t *__restrict__ row_entry, int64_t n_rows, int64_t n_blocks,
+    float *__restrict__ logits) {
+  __shared__ int32_t s_off[BLINK_MAX_QUESTIONS + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(int(threadIdx.x >> 6));
+  const int64_t per = (n_blocks + kXcds - 1) / kXcds;
+  const int64_t blk = int64_t(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (blk >= n_blocks) return;
+  const int64_t j = blk * kFlatWaves + wave;
+  const bool live = j < n_rows;
+  const int32_t id = live ? row_id[j] : 0;  // scalar: uniform address
+  for (int i = threadIdx.x; i <= n; i += 64 * kFlatWaves) s_off[i] = cand_off[i];
+  const bool id_ok = id >= 0 && id < vocab;
+  const uint16_t *wrow = w_u + int64_t(id_ok ? id : 0) * d_model;
+  const int nchunks = d_model >> 3;
+  u32x4 w[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    w[c] = u32x4{0u, 0u, 0u, 0u};
+    if (live && ch < nchunks)
+      w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + ch * 8));
+  }
+  int64_t lo = live ? row_first[j] : 0, hi = live ? row_first[j + 1] : 0;
+  if (lo < 0 || hi > total || hi < lo) lo = hi = 0;  // malformed: the row's entries stay unwritten
+  __syncthreads();
+  for (int64_t k = lo; k < hi; ++k) {
+    const int32_t e = row_entry[k];
+    if (e < 0 || e >= total) continue;
+    const int q = uniform(owner_of(s_off, n, e));
+    const int64_t row = last_row[q];
+    const bool h_ok = row >= 0 && row < hidden_rows;
+    const uint16_t *hrow = hidden + (h_ok ? row : 0) * int64_t(d_model);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      u32x4 h = u32x4{0u, 0u, 0u, 0u};
+      if (ch < nchunks) h = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = dot2(w[c][m], h[m], acc);
+    }
+    const float z = wave_sum(acc);
+    if (lane == 0) logits[e] = (id_ok && h_ok) ? z : __builtin_nanf("");
+  }
 }
 
 // One wave finishes question i from its K logits (lane holds options lane + 64 j): softmax of
@@ -291,6 +353,11 @@ struct ReadoutArgs {
   float *logits;
   float *probs;
   int32_t *argmax;
+  // Distinct-row tables of the batched form (null for the per-option form).
+  const int32_t *row_id;
+  const int32_t *row_first;
+  const int32_t *row_entry;
+  int64_t n_rows;
 };
 
 // Below this many bytes of label rows the readout is bound by launch latency: one fused
@@ -300,6 +367,20 @@ constexpr int64_t kFusedMaxBytes = int64_t(32) << 20;
 
 template <int NCH>
 hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
+  if (a.row_id) {
+    const int64_t n_blocks = (a.n_rows + kFlatWaves - 1) / kFlatWaves;
+    const int64_t grid = (n_blocks + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(label_logits_rows_kernel<NCH>, dim3(unsigned(grid)),
+                       dim3(64 * kFlatWaves), 0, stream, a.hidden, a.hidden_rows, a.d_model,
+                       a.last_row, a.w_u, a.vocab, a.off, a.n, a.total, a.row_id, a.row_first,
+                       a.row_entry, a.n_rows, n_blocks, a.logits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(label_softmax_kernel, dim3(unsigned((a.n + kWaves - 1) / kWaves)),
+                       dim3(kThreads), 0, stream, a.off, a.n, a.total, a.max_options,
+                       a.temperature, a.logits, a.probs, a.argmax);
+    return hipGetLastError();
+  }
   if (a.total * a.d_model * 2 <= kFusedMaxBytes) {
     hipLaunchKernelGGL(label_readout_fused_kernel<NCH>, dim3(unsigned(a.n)), dim3(kThreads), 0,
                        stream, a.hidden, a.hidden_rows, a.d_model, a.last_row, a.w_u, a.vocab,
@@ -324,12 +405,14 @@ typedef hipError_t (*LaunchFn)(const ReadoutArgs &, hipStream_t);
 
 }  // namespace
 
-extern "C" int blink_label_readout(const void *hidden, int64_t hidden_rows, int32_t d_model,
-                                   const int64_t *d_last_row, const void *w_u, int64_t vocab,
-                                   const int32_t *d_cand_ids, const int32_t *d_cand_off,
-                                   int32_t n_questions, int64_t total_candidates,
-                                   int32_t max_options, float temperature, float *d_logits,
-                                   float *d_probs, int32_t *d_argmax, void *stream) {
+namespace {
+
+// Checks shared by both readout entry points; returns BLINK_OK or the failing status.
+int check_common(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                 const int64_t *d_last_row, const void *w_u, int64_t vocab,
+                 const int32_t *d_cand_off, int32_t n_questions, int64_t total_candidates,
+                 int32_t max_options, float temperature, const float *d_logits,
+                 const float *d_probs, const int32_t *d_argmax) {
   using blink::fail;
   if (!(temperature > 0.f) || !isfinite(temperature))
     return fail(BLINK_E_INVALID, "temperature must be positive");
@@ -338,9 +421,8 @@ extern "C" int blink_label_readout(const void *hidden, int64_t hidden_rows, int3
   if (max_options < 1 || max_options > BLINK_MAX_OPTIONS)
     return fail(BLINK_E_LIMIT, "%d options per choice; supported 1-%d", max_options,
                 BLINK_MAX_OPTIONS);
-  if (!hidden || !d_last_row || !w_u || !d_cand_ids || !d_cand_off || !d_logits || !d_probs ||
-      !d_argmax)
-    return fail(BLINK_E_INVALID, "blink_label_readout: a pointer argument is NULL");
+  if (!hidden || !d_last_row || !w_u || !d_cand_off || !d_logits || !d_probs || !d_argmax)
+    return fail(BLINK_E_INVALID, "label readout: a pointer argument is NULL");
   if (d_model < 8 || d_model > 64 * 8 * kMaxChunksPerLane || d_model % 8)
     return fail(BLINK_E_INVALID, "d_model %d must be a multiple of 8 in 8..%d", d_model,
                 64 * 8 * kMaxChunksPerLane);
@@ -352,18 +434,61 @@ extern "C" int blink_label_readout(const void *hidden, int64_t hidden_rows, int3
                 (long long)total_candidates, n_questions, max_options);
   if (!blink::aligned16(hidden) || !blink::aligned16(w_u))
     return fail(BLINK_E_INVALID, "hidden and w_u must be 16-byte aligned");
+  return BLINK_OK;
+}
 
-  const ReadoutArgs a{static_cast<const uint16_t *>(hidden), hidden_rows, d_model, d_last_row,
-                      static_cast<const uint16_t *>(w_u), vocab, d_cand_ids, d_cand_off,
-                      n_questions, total_candidates, max_options, temperature, d_logits,
-                      d_probs, d_argmax};
-  const int nch = (d_model / 8 + 63) / 64;  // 16-byte chunks per lane
+int run(const ReadoutArgs &a, void *stream) {
+  const int nch = (a.d_model / 8 + 63) / 64;  // 16-byte chunks per lane
   static constexpr LaunchFn fns[] = {launch<1>,  launch<2>,  launch<3>,  launch<4>,
                                      launch<5>,  launch<6>,  launch<7>,  launch<8>,
                                      launch<9>,  launch<10>, launch<11>, launch<12>,
                                      launch<13>, launch<14>, launch<15>, launch<16>};
   const hipError_t err = fns[nch - 1](a, static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
-    return fail(BLINK_E_DEVICE, "blink_label_readout launch: %s", hipGetErrorString(err));
+    return blink::fail(BLINK_E_DEVICE, "label readout launch: %s", hipGetErrorString(err));
   return blink::ok();
+}
+
+}  // namespace
+
+extern "C" int blink_label_readout(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                                   const int64_t *d_last_row, const void *w_u, int64_t vocab,
+                                   const int32_t *d_cand_ids, const int32_t *d_cand_off,
+                                   int32_t n_questions, int64_t total_candidates,
+                                   int32_t max_options, float temperature, float *d_logits,
+                                   float *d_probs, int32_t *d_argmax, void *stream) {
+  const int rc = check_common(hidden, hidden_rows, d_model, d_last_row, w_u, vocab, d_cand_off,
+                              n_questions, total_candidates, max_options, temperature, d_logits,
+                              d_probs, d_argmax);
+  if (rc != BLINK_OK) return rc;
+  if (!d_cand_ids)
+    return blink::fail(BLINK_E_INVALID, "blink_label_readout: a pointer argument is NULL");
+  const ReadoutArgs a{static_cast<const uint16_t *>(hidden), hidden_rows, d_model, d_last_row,
+                      static_cast<const uint16_t *>(w_u), vocab, d_cand_ids, d_cand_off,
+                      n_questions, total_candidates, max_options, temperature, d_logits,
+                      d_probs, d_argmax, nullptr, nullptr, nullptr, 0};
+  return run(a, stream);
+}
+
+extern "C" int blink_label_readout_batched(
+    const void *hidden, int64_t hidden_rows, int32_t d_model, const int64_t *d_last_row,
+    const void *w_u, int64_t vocab, const int32_t *d_cand_off, int32_t n_questions,
+    int64_t total_candidates, int32_t max_options, const int32_t *d_row_id,
+    const int32_t *d_row_first, const int32_t *d_row_entry, int32_t n_rows, float temperature,
+    float *d_logits, float *d_probs, int32_t *d_argmax, void *stream) {
+  const int rc = check_common(hidden, hidden_rows, d_model, d_last_row, w_u, vocab, d_cand_off,
+                              n_questions, total_candidates, max_options, temperature, d_logits,
+                              d_probs, d_argmax);
+  if (rc != BLINK_OK) return rc;
+  if (!d_row_id || !d_row_first || !d_row_entry)
+    return blink::fail(BLINK_E_INVALID,
+                       "blink_label_readout_batched: a pointer argument is NULL");
+  if (n_rows < 1 || n_rows > total_candidates)
+    return blink::fail(BLINK_E_INVALID, "n_rows %d outside 1..total_candidates (%lld)", n_rows,
+                       (long long)total_candidates);
+  const ReadoutArgs a{static_cast<const uint16_t *>(hidden), hidden_rows, d_model, d_last_row,
+                      static_cast<const uint16_t *>(w_u), vocab, nullptr, d_cand_off,
+                      n_questions, total_candidates, max_options, temperature, d_logits,
+                      d_probs, d_argmax, d_row_id, d_row_first, d_row_entry, n_rows};
+  return run(a, stream);
 }

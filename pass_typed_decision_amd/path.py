@@ -21,7 +21,9 @@ from ._binding import (
     BLINK_E_INVALID,
     check_candidate_table,
     label_readout,
+    label_readout_batched,
     load_library,
+    pack_labels,
     pack_ragged,
     pack_ragged_args,
     prefix_tail_attention,
@@ -65,11 +67,17 @@ class ScoringStep:
     row tables straight into one pinned buffer that a single copy uploads, the launches use
     argument lists validated at construction, and the readout writes the probabilities and
     argmax straight into one pinned host buffer. Those host buffers are reused, so a step
-    queued with ``run(fetch=False)`` must be synchronised before the next step is packed."""
+    queued with ``run(fetch=False)`` must be synchronised before the next step is packed.
+
+    ``readout``: "per_option" (blink_label_readout, the default) or "batched"
+    (blink_label_readout_batched over the request's distinct label rows, built once here by
+    blink_pack_labels). Both give bitwise the same results; on MI355X the per-option form is
+    the faster one even where many questions share label rows."""
 
     def __init__(self, tail_len, cand_ids, cand_off, tensors: dict, n_heads_q: int,
                  n_heads_kv: int, prefix_len: int, temperature: float, scale: float,
-                 token_budget: int = TOKEN_BUDGET, max_rows: int = 0, stream=None):
+                 token_budget: int = TOKEN_BUDGET, max_rows: int = 0, stream=None,
+                 readout: str = "per_option"):
         import ctypes
 
         import torch
@@ -140,11 +148,25 @@ class ScoringStep:
             t["q"], t["k_tail"], t["v_tail"], t.get("k_prefix"), t.get("v_prefix"), self.out,
             self.d_token_offset, self.d_valid_start, pk.total_valid_tokens, self.scale,
             stream=self.stream.cuda_stream, launch=False)
-        self._read_fn = lib.blink_label_readout
-        self._read_args = label_readout(
-            t["hidden"], self.d_last_row, t["w_u"], self.cand_ids, self.cand_off,
-            self.temperature, self.max_options, self.logits, self.h_probs, self.h_argmax,
-            stream=self.stream.cuda_stream, launch=False)
+        if readout not in ("batched", "per_option"):
+            raise BlinkError(BLINK_E_INVALID, f"unknown readout form {readout!r}")
+        self.readout_form = readout
+        self.label_rows = None
+        if readout == "batched":
+            lr = self.label_rows = pack_labels(cand_ids, cand_off, vocab)
+            self.d_rows = [torch.as_tensor(a).to(dev)
+                           for a in (lr.row_id, lr.row_first, lr.row_entry)]
+            self._read_fn = lib.blink_label_readout_batched
+            self._read_args = label_readout_batched(
+                t["hidden"], self.d_last_row, t["w_u"], self.cand_off, *self.d_rows,
+                self.temperature, self.max_options, self.logits, self.h_probs, self.h_argmax,
+                stream=self.stream.cuda_stream, launch=False)
+        else:
+            self._read_fn = lib.blink_label_readout
+            self._read_args = label_readout(
+                t["hidden"], self.d_last_row, t["w_u"], self.cand_ids, self.cand_off,
+                self.temperature, self.max_options, self.logits, self.h_probs, self.h_argmax,
+                stream=self.stream.cuda_stream, launch=False)
 
     @staticmethod
     def _call(fn, args):

@@ -81,7 +81,11 @@ def run_attention(req, tensors=None, token_offset=None, tail_len=None):
     return bf16_to_f32_host(out)
 
 
-def run_readout(req, last_row=None, cand_ids=None, cand_off=None, temperature=None):
+def run_readout(req, last_row=None, cand_ids=None, cand_off=None, temperature=None,
+                batched=False, row_tables=None):
+    """Runs the readout through the C ABI: blink_label_readout, or with ``batched``
+    blink_label_readout_batched over the distinct-row tables of blink_pack_labels (or the
+    given ``row_tables`` = (row_id, row_first, row_entry))."""
     import torch
 
     import pass_typed_decision_amd as blink
@@ -101,7 +105,15 @@ def run_readout(req, last_row=None, cand_ids=None, cand_off=None, temperature=No
     probs = torch.empty_like(logits)
     argmax = torch.empty(n, dtype=torch.int32, device="cuda")
     kmax = int(np.diff(off).max())
-    blink.label_readout(hidden, d_last, w_u, d_ids, d_off, t, kmax, logits, probs, argmax)
+    if batched:
+        if row_tables is None:
+            lr = blink.pack_labels(ids, off, cfg.vocab)
+            row_tables = (lr.row_id, lr.row_first, lr.row_entry)
+        d_rows = [torch.as_tensor(np.asarray(a, np.int32)).cuda() for a in row_tables]
+        blink.label_readout_batched(hidden, d_last, w_u, d_off, *d_rows, t, kmax, logits, probs,
+                                    argmax)
+    else:
+        blink.label_readout(hidden, d_last, w_u, d_ids, d_off, t, kmax, logits, probs, argmax)
     torch.cuda.synchronize()
     return logits.cpu().numpy(), probs.cpu().numpy(), argmax.cpu().numpy()
 

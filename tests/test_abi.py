@@ -10,6 +10,7 @@ import pytest
 
 from helpers import ROOT
 from oracle.pack import pack_ragged as oracle_pack
+from oracle.readout import label_rows as oracle_label_rows
 
 HEADER = os.path.join(ROOT, "include", "blink.h")
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 1
+    assert blink.load_library().blink_abi_version() == 2
 
 
 def _compare(pk, ref):
@@ -190,3 +191,76 @@ def test_label_names():
         ["A", "B", "Z", "AA", "AB", "AZ", "BA", "IU"]
     with pytest.raises(ValueError):
         label_name(255)
+
+
+def _compare_label_rows(lr, ids, off):
+    row_id, row_first, row_entry = oracle_label_rows(ids, off)
+    assert lr.n_rows == len(row_id)
+    np.testing.assert_array_equal(lr.row_id, row_id)
+    np.testing.assert_array_equal(lr.row_first, row_first)
+    np.testing.assert_array_equal(lr.row_entry, row_entry)
+
+
+def test_pack_labels_matches_oracle_on_golden(blink):
+    import json
+
+    with open(os.path.join(ROOT, "tests", "golden", "label_rows_cases.json")) as f:
+        for case in json.load(f)["cases"]:
+            lr = blink.pack_labels(case["cand_ids"], case["cand_off"], 1000)
+            _compare_label_rows(lr, case["cand_ids"], case["cand_off"])
+
+
+def test_pack_labels_matches_oracle_random(blink):
+    rng = np.random.default_rng(321)
+    for trial in range(300):
+        n = int(rng.integers(1, 513))
+        vocab = int(rng.choice([1, 7, 64, 65, 300, 151936]))
+        kmax = int(rng.choice([1, 4, 26, 255]))
+        k = rng.integers(1, kmax + 1, size=n)
+        if trial % 3 == 0:  # the pages' form: one label table, first K per question
+            table = rng.permutation(vocab)[:kmax] if vocab >= kmax else rng.integers(0, vocab, kmax)
+            ids = np.concatenate([table[:int(x)] for x in k])
+        else:
+            ids = rng.integers(0, vocab, size=int(k.sum()))
+        off = np.concatenate([[0], np.cumsum(k)]).astype(np.int32)
+        ids = ids.astype(np.int32)
+        _compare_label_rows(blink.pack_labels(ids, off, vocab), ids, off)
+
+
+@pytest.mark.parametrize("ids, off, vocab, code, msg", [
+    ([1, 2], [0, 2, 2], 10, -2, "0 options per choice; supported 1-255"),
+    (list(range(256)), [0, 256], 300, -2, "256 options per choice; supported 1-255"),
+    ([1, 12], [0, 2], 10, -1, "option entry 1 has token id 12 outside [0, 10)"),
+    ([-1], [0, 1], 10, -1, "option entry 0 has token id -1"),
+    ([1], [0, 1], 0, -1, "vocab 0 outside"),
+    ([1], [0], 10, -2, "0 questions; supported 1-512"),
+])
+def test_pack_labels_refusals(blink, ids, off, vocab, code, msg):
+    with pytest.raises(blink.BlinkError) as e:
+        blink.pack_labels(ids, off, vocab)
+    assert e.value.code == code and msg in str(e.value)
+
+
+def _readout_batched(lib, temperature=1.0, n=2, max_options=4, d_model=256, total=4, n_rows=3,
+                     null_rows=False):
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rows = None if null_rows else fake
+    return lib.blink_label_readout_batched(fake, 10, d_model, fake, fake, 100, fake, n, total,
+                                           max_options, rows, rows, rows, n_rows, temperature,
+                                           fake, fake, fake, None)
+
+
+@pytest.mark.parametrize("kw, code, msg", [
+    (dict(temperature=0.0), -1, "temperature must be positive"),
+    (dict(n=513), -2, "513 questions; supported 1-512"),
+    (dict(max_options=256), -2, "256 options per choice; supported 1-255"),
+    (dict(d_model=12), -1, "d_model 12 must be a multiple of 8"),
+    (dict(total=9), -1, "does not fit"),
+    (dict(n_rows=0), -1, "n_rows 0 outside"),
+    (dict(n_rows=5), -1, "n_rows 5 outside"),
+    (dict(null_rows=True), -1, "a pointer argument is NULL"),
+])
+def test_readout_batched_refusals_before_launch(blink, kw, code, msg):
+    lib = blink.load_library()
+    assert _readout_batched(lib, **kw) == code
+    assert msg in lib.blink_last_error().decode()

@@ -17,20 +17,24 @@ from oracle.readout import label_readout
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("side_stream", [False, True], ids=["current", "side"])
-def test_step_matches_oracle(side_stream):
+@pytest.mark.parametrize("side_stream, readout", [(False, "per_option"), (True, "per_option"),
+                                                   (False, "batched")],
+                         ids=["current", "side", "batched"])
+def test_step_matches_oracle(side_stream, readout):
     import torch
 
     import pass_typed_decision_amd as blink
 
     cfg = synth.config(1)
-    print(f"scoring step: config 1, side stream {side_stream}", flush=True)
+    print(f"scoring step: config 1, side stream {side_stream}, readout {readout}", flush=True)
     req = Request(cfg)
     ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
     stream = torch.cuda.Stream() if side_stream else None
     step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
                              cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
-                             cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream)
+                             cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream,
+                             readout=readout)
+    assert step.readout_form == readout
     h = req.tensors
     ref = attention_full(h["q"], h["k_tail"], h["v_tail"], h.get("k_prefix"), h.get("v_prefix"),
                          req.pack["token_offset"], req.tail_len, cfg.n_heads_q, cfg.n_heads_kv,
