@@ -15,7 +15,10 @@ It follows the blink.py page (thegovind/blink-4b):
   * ``readout``   -- last-valid-row gather, FP64 dot against the offered labels' unembedding
                      rows, temperature softmax and first-index argmax ("torch engine" section:
                      _read; "answer assembly" section: softmax and answer_for), and its
-                     batched form over the distinct label rows (_read_batched).
+                     batched form over the distinct label rows (_read_batched);
+  * ``prefix``    -- shared-prefix detection, the minimum-length switch and the count of tokens
+                     computed ("torch engine" section: _shared_prefix_len, _prefill_tokens,
+                     _forward; PREFIX_MIN_TOKENS in "constants the deployment sets").
 
 Arithmetic is float64 throughout; bf16 inputs are widened exactly.
 Every function is pinned by tests under ``tests/test_oracle_*.py``; none is "parity unpinned".
@@ -30,6 +33,7 @@ from .attention import (
 )
 from .readout import label_readout, label_readout_batched, label_rows, softmax_t, MAX_OPTIONS
 from .path import score_request
+from .prefix import plan_prefix, shared_prefix_len, PREFIX_MIN_TOKENS
 
 __all__ = [
     "pack_ragged",
@@ -46,4 +50,7 @@ __all__ = [
     "label_rows",
     "softmax_t",
     "score_request",
+    "plan_prefix",
+    "shared_prefix_len",
+    "PREFIX_MIN_TOKENS",
 ]
