@@ -135,6 +135,51 @@ class TimingEvents:
         self.events = []
 
 
+def prefix_encode(cfg, tables, tensors, stream, reps: int = 5) -> dict:
+    """The request's one-off work before its steps: the shared-prefix plan (host) and the
+    prefix's own causal prefill (attention of one question of prefix_len tokens, no prefix),
+    timed with HIP events on the step stream. The step itself reads the cached prefix K/V."""
+    import torch
+
+    import pass_typed_decision_amd as blink
+    import synth
+
+    p = cfg.prefix_len
+    # Token sequences of the request (synthetic ids): the shared prefix, then each
+    # question's own tail, whose first token differs from every other question's.
+    rng = np.random.Generator(np.random.PCG64(3000 + cfg.number))
+    head = rng.integers(0, cfg.vocab, size=p).tolist()
+    seqs = [head + [int(i)] + rng.integers(0, cfg.vocab, size=int(t) - 1).tolist()
+            for i, t in enumerate(tables.tail_len)]
+    t0 = time.perf_counter()
+    plan = blink.plan_prefix(seqs)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    if plan.prefix_len != p:
+        raise RuntimeError(f"prefix plan found {plan.prefix_len} shared tokens, expected {p}")
+    q = torch.from_numpy(synth.draw_prefix_queries(cfg).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    out = torch.empty_like(q)
+    ev = TimingEvents(2 * reps, stream)
+    for _ in range(2):
+        blink.encode_prefix_attention(q, tensors["k_prefix"], tensors["v_prefix"], out, cfg.scale,
+                                      stream=None)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev.record(2 * i)
+        blink.encode_prefix_attention(q, tensors["k_prefix"], tensors["v_prefix"], out, cfg.scale,
+                                      stream=None)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
+    ev.close()
+    flops = 4.0 * cfg.head_dim * cfg.n_heads_q * p * (p + 1) / 2
+    return {"tokens": p, "attention_ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "work_per_launch": f"{flops:.4e} FLOP", "plan_host_ms": plan_ms,
+            "prefill_tokens_per_request": plan.prefill_tokens,
+            "plain_path_tokens_per_request": int(sum(len(x) for x in seqs))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +284,8 @@ def main():
                 "traffic_unit": "HBM bytes per launch", "kernel": "prefix_tail_attention_kernel",
                 "work_per_launch": f"{abytes:.4e} B"}
 
+    prefix = prefix_encode(cfg, tables, tensors, stream) if cfg.prefix_len > 0 else None
+
     baseline = None
     if not args.no_cpu_baseline:
         baseline = cpu_baseline(cfg, tables, host, args.cpu_budget)
@@ -286,6 +333,7 @@ def main():
             "label_rows": (None if step.label_rows is None else int(step.label_rows.n_rows)),
             "label_pack_host_ms_once_per_request": label_pack_ms,
         },
+        "prefix_encode_once_per_request": prefix,
         "cpu_baseline": baseline,
     }
     print(json.dumps(line), flush=True)

@@ -49,13 +49,14 @@ extern "C" {
 #define BLINK_MAX_OPTIONS 255
 #define BLINK_MAX_INPUT_TOKENS 131072
 #define BLINK_TOKEN_BUDGET 32768
+#define BLINK_PREFIX_MIN_TOKENS 256 /* shared prefixes shorter than this take the plain path */
 
 /* Message for the calling thread's last failed call; "" after a successful call. */
 const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 2
+#define BLINK_ABI_VERSION 3
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -122,6 +123,34 @@ int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, int32_t pref
 int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_off, int32_t n_questions,
                       int64_t vocab, int32_t *row_id, int32_t *row_first, int32_t *row_entry,
                       int32_t *n_rows);
+
+/*
+ * blink_plan_prefix -- host, synchronous, integer only.
+ *
+ * Shared-prefix plan of a request ("torch engine" section: _shared_prefix_len, the switch in
+ * _forward, _prefill_tokens; PREFIX_MIN_TOKENS in "constants the deployment sets"). The
+ * shared length is the number of leading tokens every sequence has in common, cut so that
+ * every sequence keeps at least one token of its own (its answer position is computed in the
+ * per-question pass); it is 0 for a single sequence. The shared path encodes that prefix
+ * once (a causal prefill: blink_prefix_tail_attention with prefix_len 0 and the prefix as the
+ * one question's tail) and runs every question's remaining tail against it; it is taken only
+ * when the shared length is at least min_prefix_tokens.
+ *
+ * Inputs (host):
+ *   tokens[seq_off[n]]   every question's full token sequence, concatenated
+ *   seq_off[n+1]         CSR offsets, seq_off[0] = 0; every sequence 1..131072 tokens
+ *                        (else BLINK_E_INVALID / BLINK_E_LIMIT, "maximum context length")
+ *   n_seqs               1..512 (else BLINK_E_LIMIT)
+ *   min_prefix_tokens    >= 1 (BLINK_PREFIX_MIN_TOKENS = 256 on the pages)
+ * Outputs (host scalars):
+ *   shared_len           the shared length
+ *   prefix_len           shared_len when the shared path is taken, else 0 (plain path)
+ *   prefill_tokens       tokens the model computes: the prefix once plus every tail on the
+ *                        shared path, every token of every sequence on the plain path
+ */
+int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, int32_t n_seqs,
+                      int32_t min_prefix_tokens, int32_t *shared_len, int32_t *prefix_len,
+                      int64_t *prefill_tokens);
 
 /*
  * blink_prefix_tail_attention -- device, asynchronous.

@@ -25,12 +25,16 @@ from ._binding import (
     TOKEN_BUDGET,
     LabelRows,
     Pack,
+    PREFIX_MIN_TOKENS,
+    PrefixPlan,
     check_candidate_table,
+    encode_prefix_attention,
     label_readout,
     label_readout_batched,
     load_library,
     pack_labels,
     pack_ragged,
+    plan_prefix,
     prefix_tail_attention,
 )
 from .path import ScoringStep, label_name
@@ -49,7 +53,11 @@ __all__ = [
     "TOKEN_BUDGET",
     "LabelRows",
     "Pack",
+    "PREFIX_MIN_TOKENS",
+    "PrefixPlan",
+    "plan_prefix",
     "check_candidate_table",
+    "encode_prefix_attention",
     "label_readout",
     "label_readout_batched",
     "load_library",

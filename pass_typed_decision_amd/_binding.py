@@ -24,6 +24,7 @@ MAX_QUESTIONS = 512
 MAX_OPTIONS = 255
 MAX_INPUT_TOKENS = 131072
 TOKEN_BUDGET = 32768
+PREFIX_MIN_TOKENS = 256
 
 # Every symbol declared in include/blink.h.
 EXPORTS = (
@@ -34,6 +35,7 @@ EXPORTS = (
     "blink_label_readout",
     "blink_pack_labels",
     "blink_label_readout_batched",
+    "blink_plan_prefix",
 )
 
 
@@ -90,6 +92,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         _P, _I64, _I32, _P, _P, _I64, _P, _I32, _I64, _I32, _P, _P, _P, _I32, _F32, _P, _P, _P,
         _P,
     ]
+    lib.blink_plan_prefix.restype = ctypes.c_int
+    lib.blink_plan_prefix.argtypes = [_PI32, _PI64, _I32, _I32, _PI32, _PI32, _PI64]
     _lib = lib
     return lib
 
@@ -177,6 +181,32 @@ def pack_ragged(tail_len, prefix_len: int = 0, token_budget: int = TOKEN_BUDGET,
                 k, tp.value, tv.value)
 
 
+@dataclass
+class PrefixPlan:
+    """Result of blink_plan_prefix."""
+
+    shared_len: int  # leading tokens common to every sequence (each keeps one of its own)
+    prefix_len: int  # shared_len on the shared path, 0 on the plain path
+    prefill_tokens: int  # tokens the model computes
+
+
+def plan_prefix(seqs, min_prefix_tokens: int = PREFIX_MIN_TOKENS) -> PrefixPlan:
+    """Shared-prefix plan of a request's token sequences (blink_plan_prefix)."""
+    lib = load_library()
+    lens = [len(s) for s in seqs]
+    off = np.zeros(len(lens) + 1, np.int64)
+    off[1:] = np.cumsum(lens)
+    flat = (np.concatenate([np.asarray(s, np.int32) for s in seqs]) if seqs and off[-1]
+            else np.zeros(1, np.int32))
+    flat = np.ascontiguousarray(flat, dtype=np.int32)
+    shared, prefix = ctypes.c_int32(0), ctypes.c_int32(0)
+    prefill = ctypes.c_int64(0)
+    _check(lib.blink_plan_prefix(_ptr(flat, ctypes.c_int32), _ptr(off, ctypes.c_int64), len(lens),
+                                 int(min_prefix_tokens), ctypes.byref(shared),
+                                 ctypes.byref(prefix), ctypes.byref(prefill)))
+    return PrefixPlan(shared.value, prefix.value, prefill.value)
+
+
 def _stream(stream):
     if stream is not None:
         return ctypes.c_void_p(int(stream))
@@ -245,6 +275,31 @@ def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offs
     if not launch:
         return args
     _check(lib.blink_prefix_tail_attention(*args))
+
+
+def encode_prefix_attention(q, k, v, out, scale: float, stream=None):
+    """Attention of the shared prefix's own causal prefill, encoded once per request
+    ("torch engine" section, _forward_shared: the batch-1 forward over the prefix tokens).
+    It is blink_prefix_tail_attention with no prefix and the whole prefix as the tail of a
+    single question. q/out [L, H_q, D], k/v [L, H_kv, D] (bf16, device). Returns the two
+    small device row tables the launch reads (keep them until the stream has finished)."""
+    import torch
+
+    length = int(q.shape[0])
+    if length < 1:
+        raise BlinkError(BLINK_E_INVALID, "the prefix needs at least one token")
+    token_offset = torch.zeros(1, dtype=torch.int64, device=q.device)
+    valid_start = torch.tensor([0, length], dtype=torch.int32, device=q.device)
+    if stream is not None:
+        s = torch.cuda.ExternalStream(int(stream)) if not isinstance(stream, torch.cuda.Stream) \
+            else stream
+        s.wait_stream(torch.cuda.current_stream())
+        token_offset.record_stream(s)
+        valid_start.record_stream(s)
+        stream = s.cuda_stream
+    prefix_tail_attention(q, k, v, None, None, out, token_offset, valid_start, length, scale,
+                          stream=stream)
+    return token_offset, valid_start
 
 
 def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,

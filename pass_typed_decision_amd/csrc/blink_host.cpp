@@ -10,6 +10,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <climits>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -184,5 +185,48 @@ extern "C" int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_of
   for (int32_t j = 0; j <= u; ++j) row_first[j] = cursor[j];
   for (int32_t e = 0; e < total; ++e) row_entry[cursor[col[e]]++] = e;
   *n_rows = u;
+  return blink::ok();
+}
+
+// Shared-prefix plan of a request (blink.py page, "torch engine" section: _shared_prefix_len,
+// _forward's switch to the shared path, _prefill_tokens). The shared length is found by
+// walking token positions while every sequence agrees with the first one, and is cut so
+// that every sequence keeps at least one token of its own.
+extern "C" int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, int32_t n_seqs,
+                                 int32_t min_prefix_tokens, int32_t *shared_len,
+                                 int32_t *prefix_len, int64_t *prefill_tokens) {
+  using blink::fail;
+  if (!tokens || !seq_off || !shared_len || !prefix_len || !prefill_tokens)
+    return fail(BLINK_E_INVALID, "blink_plan_prefix: a pointer argument is NULL");
+  if (n_seqs < 1 || n_seqs > BLINK_MAX_QUESTIONS)
+    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_seqs, BLINK_MAX_QUESTIONS);
+  if (min_prefix_tokens < 1)
+    return fail(BLINK_E_INVALID, "the minimum shared prefix must be at least 1");
+  if (seq_off[0] != 0) return fail(BLINK_E_INVALID, "sequence offsets must start at 0");
+  int64_t shortest = INT64_MAX, total = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int64_t len = seq_off[i + 1] - seq_off[i];
+    if (len < 1) return fail(BLINK_E_INVALID, "sequence %d needs at least one token", i);
+    if (len > BLINK_MAX_INPUT_TOKENS)
+      return fail(BLINK_E_LIMIT,
+                  "question %d renders to %lld tokens, over the maximum context length of %d", i,
+                  (long long)len, BLINK_MAX_INPUT_TOKENS);
+    shortest = std::min(shortest, len);
+    total += len;
+  }
+  int64_t p = 0;
+  if (n_seqs >= 2) {
+    const int32_t *first = tokens + seq_off[0];
+    // Position by position; stop at the first mismatch or at the shortest sequence's last
+    // token, which stays its own.
+    for (bool same = true; same && p < shortest - 1; p += same) {
+      const int32_t t = first[p];
+      for (int i = 1; i < n_seqs && same; ++i) same = tokens[seq_off[i] + p] == t;
+    }
+  }
+  *shared_len = int32_t(p);
+  const bool use = p > 0 && p >= min_prefix_tokens;
+  *prefix_len = use ? int32_t(p) : 0;
+  *prefill_tokens = use ? total - int64_t(n_seqs - 1) * p : total;
   return blink::ok();
 }

@@ -157,3 +157,11 @@ def draw_tensors(cfg: Config, rng: np.random.Generator, total_padded_tokens: int
         if name in wanted:
             out[name] = arr
     return out
+
+
+def draw_prefix_queries(cfg: Config, seed: int | None = None) -> np.ndarray:
+    """Query rows of the shared prefix itself, bf16 bits [prefix_len, H_q, D] ~ N(0, 1), from
+    their own PCG64 stream (seed 2000 + workload number by default). They are the inputs of
+    the prefix's own causal prefill; the request's draws are not disturbed."""
+    rng = np.random.Generator(np.random.PCG64(2000 + cfg.number if seed is None else seed))
+    return _normal_bf16(rng, (cfg.prefix_len, cfg.n_heads_q, cfg.head_dim), 1.0)

@@ -11,6 +11,7 @@ import pytest
 from helpers import ROOT
 from oracle.pack import pack_ragged as oracle_pack
 from oracle.readout import label_rows as oracle_label_rows
+from oracle.prefix import plan_prefix as oracle_plan_prefix
 
 HEADER = os.path.join(ROOT, "include", "blink.h")
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 2
+    assert blink.load_library().blink_abi_version() == 3
 
 
 def _compare(pk, ref):
@@ -264,3 +265,49 @@ def test_readout_batched_refusals_before_launch(blink, kw, code, msg):
     lib = blink.load_library()
     assert _readout_batched(lib, **kw) == code
     assert msg in lib.blink_last_error().decode()
+
+
+def test_plan_prefix_matches_oracle_on_golden(blink):
+    import json
+
+    with open(os.path.join(ROOT, "tests", "golden", "prefix_cases.json")) as f:
+        for case in json.load(f)["cases"]:
+            got = blink.plan_prefix(case["seqs"], case["min_prefix_tokens"])
+            assert (got.shared_len, got.prefix_len, got.prefill_tokens) == (
+                case["shared"], case["prefix_len"], case["prefill_tokens"]), case["name"]
+
+
+def test_plan_prefix_matches_oracle_random(blink):
+    rng = np.random.default_rng(77)
+    for _ in range(500):
+        n = int(rng.integers(1, 20))
+        vocab = int(rng.choice([2, 5, 1000]))
+        head = rng.integers(0, vocab, size=int(rng.integers(0, 600))).tolist()
+        seqs = []
+        for _ in range(n):
+            cut = int(rng.integers(max(0, len(head) - 3), len(head) + 1))
+            tail = rng.integers(0, vocab, size=int(rng.integers(0, 6))).tolist()
+            seq = head[:cut] + tail
+            seqs.append(seq if seq else [int(rng.integers(0, vocab))])
+        m = int(rng.choice([1, 2, 256, 10**6]))
+        got = blink.plan_prefix(seqs, m)
+        assert (got.shared_len, got.prefix_len, got.prefill_tokens) == oracle_plan_prefix(seqs, m)
+
+
+def test_plan_prefix_at_the_context_limit(blink):
+    head = list(range(131071))
+    got = blink.plan_prefix([head + [1], head + [2]])
+    assert (got.shared_len, got.prefix_len, got.prefill_tokens) == (131071, 131071, 131073)
+
+
+@pytest.mark.parametrize("seqs, m, code, msg", [
+    ([], 256, -2, "0 questions; supported 1-512"),
+    ([[1]] * 513, 256, -2, "513 questions; supported 1-512"),
+    ([[1, 2], []], 256, -1, "sequence 1 needs at least one token"),
+    ([[1, 2]], 0, -1, "the minimum shared prefix must be at least 1"),
+    ([[0] * 131073], 256, -2, "question 0 renders to 131073 tokens, over the maximum context length"),
+])
+def test_plan_prefix_refusals(blink, seqs, m, code, msg):
+    with pytest.raises(blink.BlinkError) as e:
+        blink.plan_prefix(seqs, m)
+    assert e.value.code == code and msg in str(e.value)
