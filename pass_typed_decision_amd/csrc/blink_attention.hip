@@ -49,12 +49,14 @@
 //    on which other rows share its wave.
 //  * Prefix tiles first (unmasked except the last partial tile), then the tail tiles of each
 //    question the unit touches, masked per lane (same question and key <= position).
-//  * Two tile paths. Whole prefix tiles for a wave whose rows all have their reference take a
+//  * Two tile paths. Whole tiles for a wave whose rows all have their reference take a
 //    branch-free path with no row maxima: both 32-key score blocks, then exp2, bf16, row sums
 //    and PV, with the next tiles' loads issued between the score MFMAs, which run at raised
-//    wave priority so the matrix pipe is fed ahead of other waves' softmax. Everything else
-//    (masked tail tiles, the last partial prefix tile, a row's first tile) takes the general
-//    path, one 32-key block at a time.
+//    wave priority so the matrix pipe is fed ahead of other waves' softmax. A whole tile is a
+//    full prefix tile, or a tail tile of the wave's one question whose 64 keys all lie at or
+//    before every row of the wave (in a long causal tail, such as the prefix's own prefill,
+//    nearly all of them). Everything else (tiles that cut the causal diagonal, the last partial
+//    prefix tile, a row's first tile) takes the general path, one 32-key block at a time.
 //  * The request's row tables (valid_start, token_offset) are copied into LDS when the
 //    workgroup starts, so every lookup on the way to the first tile is an LDS read.
 //  * Output rows go through LDS (two idle stages of the ring, half a row at a time) so that
@@ -64,6 +66,10 @@
 //    the 8 XCDs (dispatch is round-robin over XCDs) streams one head's prefix K/V through its
 //    own L2. The rows left for the last round of workgroups are re-cut into smaller units
 //    (unit_split) so that that round covers every CU.
+//  * Units are dispatched from the last row to the first. A causal row sees one more key than
+//    the row before it, so later units carry more work; starting the heaviest first lets the
+//    light ones fill in at the end (in a 65536-token causal prefill, 7-9% faster than row
+//    order). The re-cut small units then run first, still one per CU.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -114,6 +120,7 @@ struct Args {
   float scale_log2;
   int64_t full_units;  // per KV head: units [0, full_units) hold kRowsPerUnit rows each,
   int small_rows;      // later units small_rows each (see unit_split)
+  int64_t n_units;     // per KV head
 };
 
 template <int D>
@@ -522,6 +529,7 @@ struct RowTables {
 struct WaveSpan {
   bool active;     // the wave has at least one real row
   int qa, qz, posz;  // questions the wave's rows touch; last row's position in qz
+  int posa;          // first row's position in qa
 };
 
 template <int D>
@@ -583,8 +591,11 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     bool fresh = false;  // some row of this wave has not seen a visible key yet
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) fresh |= rs[qb].m == -INFINITY;
-    const bool fast = !max_only && cur.q < 0 && cur.kstart + kTileKeys <= a.prefix_len &&
-                      !__builtin_amdgcn_ballot_w64(fresh);
+    // A whole tile: every key visible to every row of the wave (see the two tile paths).
+    const bool whole = cur.q < 0 ? cur.kstart + kTileKeys <= a.prefix_len
+                                 : cur.q == ws.qa && ws.qa == ws.qz &&
+                                       cur.kstart + kTileKeys <= ws.posa + 1;
+    const bool fast = !max_only && whole && !__builtin_amdgcn_ballot_w64(fresh);
     if (active && fast) {
       compute_tile_fast<D>(sm.k[stage] + klane, sm.v[stage] + vlane, qf, o, rs, ra,
                            sm.k[stage2], sm.v[stage2], wave, plan);
@@ -728,7 +739,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const int col = lane & 31, half = lane >> 5;
   const int G = a.group;
   const int g = int(blockIdx.x % unsigned(a.hkv));
-  const int64_t unit = blockIdx.x / unsigned(a.hkv);
+  const int64_t unit = a.n_units - 1 - int64_t(blockIdx.x / unsigned(a.hkv));  // heaviest first
+  if (unit < 0) return;  // uniform; the grid holds exactly n_units units per head
 
   for (int i = tid; i <= a.n; i += kThreads) {
     sm.tab.start[i] = a.valid_start[i];
@@ -755,10 +767,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   }
   const int64_t wr0 = row0 + wave * kRowsPerWave;
   const bool wave_active = wr0 < row_end;
-  int wqa = 0, wqz = -1, wposz = -1;
+  int wqa = 0, wqz = -1, wposz = -1, wposa = 0;
   if (wave_active) {
     const int64_t c0 = wr0 / G, cz = (min(wr0 + kRowsPerWave, row_end) - 1) / G;
     wqa = uniform(find_question(sm.tab.start, a.n, c0));
+    wposa = uniform(int(c0 - sm.tab.start[wqa]));
     wqz = uniform(find_question(sm.tab.start, a.n, cz));
     wposz = uniform(int(cz - sm.tab.start[wqz]));
   }
@@ -811,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const RowTables rt{rq, rpos};
   // This wave's area in stages 0 and 1 for staging its output rows (used after the tiles).
   char *ostage = out_stage<D>(sm, 0, wave);
-  const WaveSpan ws{wave_active, wqa, wqz, wposz};
+  const WaveSpan ws{wave_active, wqa, wqz, wposz, wposa};
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
   init_rows<D>(o, rs, true);
@@ -945,6 +958,7 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
   a.scale_log2 = scale * kLog2e;
   a.full_units = full_units;
   a.small_rows = small_rows;
+  a.n_units = units;
 
   (void)hipGetLastError();
   const hipError_t err = head_dim == 64 ? launch<64>(a, static_cast<hipStream_t>(stream))
