@@ -18,7 +18,9 @@ It follows the blink.py page (thegovind/blink-4b):
                      batched form over the distinct label rows (_read_batched);
   * ``prefix``    -- shared-prefix detection, the minimum-length switch and the count of tokens
                      computed ("torch engine" section: _shared_prefix_len, _prefill_tokens,
-                     _forward; PREFIX_MIN_TOKENS in "constants the deployment sets").
+                     _forward; PREFIX_MIN_TOKENS in "constants the deployment sets");
+  * ``answers``   -- typed answers from the option probabilities ("answer assembly" section:
+                     answer_for).
 
 Arithmetic is float64 throughout; bf16 inputs are widened exactly.
 Every function is pinned by tests under ``tests/test_oracle_*.py``; none is "parity unpinned".
@@ -34,6 +36,7 @@ from .attention import (
 from .readout import label_readout, label_readout_batched, label_rows, softmax_t, MAX_OPTIONS
 from .path import score_request
 from .prefix import plan_prefix, shared_prefix_len, PREFIX_MIN_TOKENS
+from .answers import answer_for, assemble
 
 __all__ = [
     "pack_ragged",
@@ -53,4 +56,6 @@ __all__ = [
     "plan_prefix",
     "shared_prefix_len",
     "PREFIX_MIN_TOKENS",
+    "answer_for",
+    "assemble",
 ]
