@@ -56,7 +56,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 3
+#define BLINK_ABI_VERSION 4
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -251,6 +251,34 @@ int blink_label_readout_batched(const void *hidden, int64_t hidden_rows, int32_t
                                 const int32_t *d_row_entry, int32_t n_rows, float temperature,
                                 float *d_logits, float *d_probs, int32_t *d_argmax,
                                 void *stream);
+
+/*
+ * blink_assemble_answers -- host, synchronous.
+ *
+ * Typed answers from the readout's probabilities ("answer assembly" section, answer_for;
+ * "rendering" section, question_options). Each question's probabilities are renormalised to
+ * sum to one (a zero sum divides by one), in double precision, then by question type:
+ *   BLINK_ANSWER_CHOICE  choice = the first most probable option; value = its probability;
+ *                        confidence = (p_best - 1/K) / (1 - 1/K), 1 for K = 1
+ *   BLINK_ANSWER_NOUL    options are (yes, no), K = 2; value = p(yes); choice = -1;
+ *                        confidence = NaN (the pages give none)
+ *   BLINK_ANSWER_SCORE   options are the levels 0..K-1, 2 <= K <= 10; value = sum_k k p_k;
+ *                        choice = the first most probable level; confidence as for a choice,
+ *                        clipped to [0, 1]
+ *
+ *   probs[total]      host copy of the readout's probabilities (CSR by question)
+ *   cand_off[n+1]     CSR offsets (cand_off[0] = 0, 1 <= K_i <= 255)
+ *   qtype[n]          BLINK_ANSWER_* of each question (else BLINK_E_INVALID; a noul question
+ *                     with K != 2 or a score with K outside 2..10 is BLINK_E_INVALID)
+ *   n_questions       1..512
+ *   choice[n], confidence[n], value[n]   outputs (host)
+ */
+#define BLINK_ANSWER_CHOICE 0
+#define BLINK_ANSWER_NOUL 1
+#define BLINK_ANSWER_SCORE 2
+int blink_assemble_answers(const float *probs, const int32_t *cand_off, const int32_t *qtype,
+                           int32_t n_questions, int32_t *choice, double *confidence,
+                           double *value);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,10 @@ from ._binding import (
     Pack,
     PREFIX_MIN_TOKENS,
     PrefixPlan,
+    ANSWER_CHOICE,
+    ANSWER_NOUL,
+    ANSWER_SCORE,
+    assemble_answers,
     check_candidate_table,
     encode_prefix_attention,
     label_readout,
@@ -56,6 +60,10 @@ __all__ = [
     "PREFIX_MIN_TOKENS",
     "PrefixPlan",
     "plan_prefix",
+    "ANSWER_CHOICE",
+    "ANSWER_NOUL",
+    "ANSWER_SCORE",
+    "assemble_answers",
     "check_candidate_table",
     "encode_prefix_attention",
     "label_readout",

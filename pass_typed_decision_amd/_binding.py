@@ -36,6 +36,7 @@ EXPORTS = (
     "blink_pack_labels",
     "blink_label_readout_batched",
     "blink_plan_prefix",
+    "blink_assemble_answers",
 )
 
 
@@ -92,6 +93,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         _P, _I64, _I32, _P, _P, _I64, _P, _I32, _I64, _I32, _P, _P, _P, _I32, _F32, _P, _P, _P,
         _P,
     ]
+    lib.blink_assemble_answers.restype = ctypes.c_int
+    lib.blink_assemble_answers.argtypes = [
+        ctypes.POINTER(ctypes.c_float), _PI32, _PI32, _I32, _PI32,
+        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.blink_plan_prefix.restype = ctypes.c_int
     lib.blink_plan_prefix.argtypes = [_PI32, _PI64, _I32, _I32, _PI32, _PI32, _PI64]
     _lib = lib
@@ -205,6 +210,33 @@ def plan_prefix(seqs, min_prefix_tokens: int = PREFIX_MIN_TOKENS) -> PrefixPlan:
                                  int(min_prefix_tokens), ctypes.byref(shared),
                                  ctypes.byref(prefix), ctypes.byref(prefill)))
     return PrefixPlan(shared.value, prefix.value, prefill.value)
+
+
+ANSWER_CHOICE, ANSWER_NOUL, ANSWER_SCORE = 0, 1, 2
+
+
+def assemble_answers(probs, cand_off, qtype):
+    """Typed answers of a request (blink_assemble_answers): returns (choice int32 [n],
+    confidence float64 [n], value float64 [n])."""
+    lib = load_library()
+    p = np.ascontiguousarray(np.asarray(probs, dtype=np.float32))
+    off = np.ascontiguousarray(np.asarray(cand_off, dtype=np.int32))
+    t = np.ascontiguousarray(np.asarray(qtype, dtype=np.int32))
+    n = int(t.shape[0])
+    if off.shape[0] != n + 1 or (n and int(off[-1]) != p.shape[0]):
+        raise BlinkError(BLINK_E_INVALID, "offsets must have n + 1 entries ending at len(probs)")
+    cap = max(n, 1)
+    choice = np.zeros(cap, np.int32)
+    conf = np.zeros(cap, np.float64)
+    value = np.zeros(cap, np.float64)
+    src_p = p if p.size else np.zeros(1, np.float32)
+    src_t = t if n else np.zeros(1, np.int32)
+    _check(lib.blink_assemble_answers(
+        src_p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(off, ctypes.c_int32),
+        _ptr(src_t, ctypes.c_int32), n, _ptr(choice, ctypes.c_int32),
+        conf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        value.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return choice[:n], conf[:n], value[:n]
 
 
 def _stream(stream):

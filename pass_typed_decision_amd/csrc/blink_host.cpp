@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -228,5 +229,63 @@ extern "C" int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, 
   const bool use = p > 0 && p >= min_prefix_tokens;
   *prefix_len = use ? int32_t(p) : 0;
   *prefill_tokens = use ? total - int64_t(n_seqs - 1) * p : total;
+  return blink::ok();
+}
+
+// Typed answers from one request's option probabilities (blink.py page, "answer assembly"
+// section, answer_for): renormalise each question's probabilities (a zero sum divides by
+// one), then a choice takes its first most probable option and the confidence
+// (p_best - 1/K) / (1 - 1/K) (1 for a single option); a noul question (options yes, no)
+// gives the probability of yes; a score question (levels 0..K-1, 2 <= K <= 10) gives the
+// expected level, its first most probable level and the same confidence clipped to [0, 1].
+extern "C" int blink_assemble_answers(const float *probs, const int32_t *cand_off,
+                                      const int32_t *qtype, int32_t n_questions,
+                                      int32_t *choice, double *confidence, double *value) {
+  using blink::fail;
+  if (!probs || !cand_off || !qtype || !choice || !confidence || !value)
+    return fail(BLINK_E_INVALID, "blink_assemble_answers: a pointer argument is NULL");
+  if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
+    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
+  if (cand_off[0] != 0) return fail(BLINK_E_INVALID, "candidate offsets must start at 0");
+  for (int i = 0; i < n_questions; ++i) {
+    const int64_t k = int64_t(cand_off[i + 1]) - cand_off[i];
+    if (k < 1 || k > BLINK_MAX_OPTIONS)
+      return fail(BLINK_E_LIMIT, "%lld options per choice; supported 1-%d", (long long)k,
+                  BLINK_MAX_OPTIONS);
+    if (qtype[i] == BLINK_ANSWER_NOUL && k != 2)
+      return fail(BLINK_E_INVALID, "question %d: a noul question offers exactly yes and no", i);
+    if (qtype[i] == BLINK_ANSWER_SCORE && (k < 2 || k > 10))
+      return fail(BLINK_E_INVALID, "question %d: a score takes 2 to 10 levels", i);
+    if (qtype[i] != BLINK_ANSWER_CHOICE && qtype[i] != BLINK_ANSWER_NOUL &&
+        qtype[i] != BLINK_ANSWER_SCORE)
+      return fail(BLINK_E_INVALID, "question %d: unknown question type %d", i, qtype[i]);
+  }
+  for (int i = 0; i < n_questions; ++i) {
+    const float *p = probs + cand_off[i];
+    const int k = cand_off[i + 1] - cand_off[i];
+    double z = 0.0;
+    for (int j = 0; j < k; ++j) z += double(p[j]);
+    if (z == 0.0) z = 1.0;
+    int best = 0;
+    for (int j = 1; j < k; ++j)
+      if (double(p[j]) / z > double(p[best]) / z) best = j;
+    const double pb = double(p[best]) / z;
+    const double conf = k > 1 ? (pb - 1.0 / k) / (1.0 - 1.0 / k) : 1.0;
+    if (qtype[i] == BLINK_ANSWER_CHOICE) {
+      choice[i] = best;
+      confidence[i] = conf;
+      value[i] = pb;
+    } else if (qtype[i] == BLINK_ANSWER_NOUL) {
+      choice[i] = -1;
+      confidence[i] = NAN;
+      value[i] = double(p[0]) / z;
+    } else {
+      double ev = 0.0;
+      for (int j = 0; j < k; ++j) ev += j * (double(p[j]) / z);
+      choice[i] = best;
+      confidence[i] = std::min(1.0, std::max(0.0, conf));
+      value[i] = ev;
+    }
+  }
   return blink::ok();
 }

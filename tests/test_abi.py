@@ -12,6 +12,7 @@ from helpers import ROOT
 from oracle.pack import pack_ragged as oracle_pack
 from oracle.readout import label_rows as oracle_label_rows
 from oracle.prefix import plan_prefix as oracle_plan_prefix
+from oracle.answers import assemble as oracle_assemble
 
 HEADER = os.path.join(ROOT, "include", "blink.h")
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 3
+    assert blink.load_library().blink_abi_version() == 4
 
 
 def _compare(pk, ref):
@@ -310,4 +311,53 @@ def test_plan_prefix_at_the_context_limit(blink):
 def test_plan_prefix_refusals(blink, seqs, m, code, msg):
     with pytest.raises(blink.BlinkError) as e:
         blink.plan_prefix(seqs, m)
+    assert e.value.code == code and msg in str(e.value)
+
+
+def _compare_answers(blink, probs, off, types):
+    p32 = np.asarray(probs, np.float32)
+    choice, conf, value = blink.assemble_answers(p32, off, types)
+    ref = oracle_assemble(types, p32.astype(np.float64), off)
+    for i, (c, f, v) in enumerate(ref):
+        assert choice[i] == c, i
+        if f is None:
+            assert np.isnan(conf[i])
+        else:
+            assert abs(conf[i] - f) <= 1e-12, i
+        assert abs(value[i] - v) <= 1e-12, i
+
+
+def test_assemble_answers_matches_oracle_on_golden(blink):
+    import json
+
+    with open(os.path.join(ROOT, "tests", "golden", "answer_cases.json")) as f:
+        for case in json.load(f)["cases"]:
+            _compare_answers(blink, case["probs"], [0, len(case["probs"])], [case["type"]])
+
+
+def test_assemble_answers_matches_oracle_random(blink):
+    rng = np.random.default_rng(99)
+    for _ in range(200):
+        n = int(rng.integers(1, 513))
+        types = rng.integers(0, 3, size=n)
+        k = np.where(types == 1, 2, np.where(types == 2, rng.integers(2, 11, size=n),
+                                             rng.integers(1, 256, size=n)))
+        off = np.concatenate([[0], np.cumsum(k)]).astype(np.int32)
+        probs = np.concatenate([rng.dirichlet(np.ones(int(x))) for x in k])
+        if rng.random() < 0.3:  # exact ties in float32
+            probs = np.round(probs * 4) / 4
+        _compare_answers(blink, probs, off, types.astype(np.int32))
+
+
+@pytest.mark.parametrize("probs, off, types, code, msg", [
+    ([], [0], [], -2, "0 questions; supported 1-512"),
+    ([0.2, 0.3, 0.5], [0, 3], [1], -1, "a noul question offers exactly yes and no"),
+    ([1.0], [0, 1], [2], -1, "a score takes 2 to 10 levels"),
+    ([0.1] * 11, [0, 11], [2], -1, "a score takes 2 to 10 levels"),
+    ([0.5, 0.5], [0, 2], [5], -1, "unknown question type 5"),
+    ([0.5, 0.5], [0, 2, 2], [0, 0], -2, "0 options per choice"),
+])
+def test_assemble_answers_refusals(blink, probs, off, types, code, msg):
+    with pytest.raises(blink.BlinkError) as e:
+        blink.assemble_answers(probs, off, types)
     assert e.value.code == code and msg in str(e.value)

@@ -56,3 +56,37 @@ def test_step_matches_oracle(side_stream, readout):
         assert attn_err <= ATTN_TOL
         assert prob_err <= PROB_TOL
         check_argmax(z, req.tables.cand_off, a, arg)
+
+
+def test_typed_answers_from_the_step():
+    # The step's GPU probabilities, assembled into typed answers on the host, against the
+    # oracle's answers from its FP64 probabilities ("answer assembly" section, answer_for).
+    import pass_typed_decision_amd as blink
+    from oracle.answers import assemble
+
+    cfg = synth.config(1)
+    req = Request(cfg)
+    ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
+    step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows)
+    probs, _ = step.run()
+    off = req.tables.cand_off
+    k = np.diff(off)
+    types = np.where(k == 2, blink.ANSWER_NOUL,
+                     np.where(np.arange(len(k)) % 2 == 1, blink.ANSWER_SCORE,
+                              blink.ANSWER_CHOICE)).astype(np.int32)
+    choice, conf, value = blink.assemble_answers(probs, off, types)
+    _, p, _ = label_readout(req.tensors["hidden"], req.pack["last_row"], req.tensors["w_u"],
+                            req.tables.cand_ids, off, cfg.temperature)
+    ref = assemble(types, p, off)
+    print(f"  typed answers for types {types.tolist()}", flush=True)
+    for i, (c, f, v) in enumerate(ref):
+        assert abs(value[i] - v) <= 10 * PROB_TOL
+        if f is None:
+            assert choice[i] == -1 and np.isnan(conf[i])
+            continue
+        assert abs(conf[i] - f) <= 10 * PROB_TOL
+        q = np.sort(p[off[i]:off[i + 1]])
+        if len(q) == 1 or q[-1] - q[-2] > 1e-5:
+            assert choice[i] == c
