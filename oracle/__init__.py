@@ -32,6 +32,7 @@ from .attention import (
     attention_full,
     attention_decomposed,
     attention_rows,
+    attention_grouped,
 )
 from .readout import label_readout, label_readout_batched, label_rows, softmax_t, MAX_OPTIONS
 from .path import score_request
@@ -48,6 +49,7 @@ __all__ = [
     "attention_full",
     "attention_decomposed",
     "attention_rows",
+    "attention_grouped",
     "label_readout",
     "label_readout_batched",
     "label_rows",

@@ -148,3 +148,24 @@ def attention_rows(q, k_tail, v_tail, k_prefix, v_prefix, token_offset, tail_len
             w = np.exp(s - s.max())
             out[r] = (w @ values[: p + t + 1]) / w.sum()
     return out
+
+
+def attention_grouped(q, k_tail, v_tail, k_prefix, v_prefix, token_offset, tail_len,
+                      request_first, prefix_start, prefix_len, n_heads_q, n_heads_kv, scale):
+    """Several requests in one packed buffer, each question attending to its own request's
+    prefix (rows prefix_start[r] .. prefix_start[r] + prefix_len[r] of k/v_prefix) and to its
+    own tail: the plain full-sequence definition applied request by request ("public entry
+    point" section of the blink.py page: the questions of several requests share one call)."""
+    q = np.asarray(q)
+    out = np.full((q.shape[0], n_heads_q, q.shape[2]), np.nan)
+    for r in range(len(request_first) - 1):
+        qs = range(int(request_first[r]), int(request_first[r + 1]))
+        p0, pl = int(prefix_start[r]), int(prefix_len[r])
+        kp = None if pl == 0 else np.asarray(k_prefix)[p0:p0 + pl]
+        vp = None if pl == 0 else np.asarray(v_prefix)[p0:p0 + pl]
+        part = attention_full(q, k_tail, v_tail, kp, vp, token_offset, tail_len, n_heads_q,
+                              n_heads_kv, scale, questions=qs)
+        for i in qs:
+            off, n = int(token_offset[i]), int(tail_len[i])
+            out[off:off + n] = part[off:off + n]
+    return out

@@ -179,3 +179,63 @@ def test_bf16_inputs_are_widened_exactly():
     assert bf16_to_f64(synth.f32_to_bf16_bits(halfway))[0] == 1.0
     above = np.array([1.0 + 2.0 ** -8 + 2.0 ** -20], np.float32)
     assert bf16_to_f64(synth.f32_to_bf16_bits(above))[0] == 1.0 + 2.0 ** -7
+
+
+def _grouped_case(seed, prefixes=(0, 5, 9), questions=(2, 1, 3), d=8, hq=4, hkv=2):
+    rng = np.random.default_rng(seed)
+    tails = [rng.integers(1, 7, size=n).tolist() for n in questions]
+    lens = [t for ts in tails for t in ts]
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    t_pad = int(sum(lens))
+    q = rng.standard_normal((t_pad, hq, d))
+    kt = rng.standard_normal((t_pad, hkv, d))
+    vt = rng.standard_normal((t_pad, hkv, d))
+    rows = max(1, sum(prefixes))
+    kp = rng.standard_normal((rows, hkv, d))
+    vp = rng.standard_normal((rows, hkv, d))
+    first = np.concatenate([[0], np.cumsum(questions)]).astype(int)
+    pstart = np.concatenate([[0], np.cumsum(prefixes)[:-1]]).astype(int)
+    return q, kt, vt, kp, vp, off, lens, first, pstart, list(prefixes), hq, hkv
+
+
+def test_grouped_with_one_request_is_the_plain_call():
+    from oracle.attention import attention_grouped
+
+    q, kt, vt, kp, vp, off, lens, _, _, _, hq, hkv = _grouped_case(1, prefixes=(7,),
+                                                                    questions=(4,))
+    got = attention_grouped(q, kt, vt, kp, vp, off, lens, [0, 4], [0], [7], hq, hkv, 0.3)
+    ref = attention_full(q, kt, vt, kp[:7], vp[:7], off, lens, hq, hkv, 0.3)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_grouped_requests_see_only_their_own_prefix():
+    from oracle.attention import attention_grouped
+
+    q, kt, vt, kp, vp, off, lens, first, pstart, plen, hq, hkv = _grouped_case(2)
+    got = attention_grouped(q, kt, vt, kp, vp, off, lens, first, pstart, plen, hq, hkv, 0.3)
+    for r in range(3):
+        for i in range(first[r], first[r + 1]):
+            o, n = int(off[i]), lens[i]
+            # the question alone, its request's prefix concatenated in front (plain causal)
+            pre_k = kp[pstart[r]:pstart[r] + plen[r]]
+            pre_v = vp[pstart[r]:pstart[r] + plen[r]]
+            full_k = np.concatenate([pre_k, kt[o:o + n]])
+            full_v = np.concatenate([pre_v, vt[o:o + n]])
+            ref = attention_full(np.concatenate([np.zeros((plen[r], hq, q.shape[2])), q[o:o + n]]),
+                                 full_k, full_v, None, None, [0], [plen[r] + n], hq, hkv, 0.3)
+            np.testing.assert_allclose(got[o:o + n], ref[plen[r]:], atol=1e-12)
+    # a wrong prefix (the next request's) changes the rows of a request that has a prefix
+    bad = attention_grouped(q, kt, vt, kp, vp, off, lens, first, [pstart[2]] * 3, plen, hq,
+                            hkv, 0.3)
+    o1 = int(off[first[1]])
+    assert np.abs(bad[o1] - got[o1]).max() > 1e-6
+
+
+def test_grouped_requests_may_share_prefix_rows():
+    from oracle.attention import attention_grouped
+
+    q, kt, vt, kp, vp, off, lens, first, _, _, hq, hkv = _grouped_case(3, prefixes=(6, 6, 6))
+    shared = attention_grouped(q, kt, vt, kp, vp, off, lens, first, [0, 0, 0], [6, 6, 6], hq,
+                               hkv, 0.3)
+    one = attention_full(q, kt, vt, kp[:6], vp[:6], off, lens, hq, hkv, 0.3)
+    np.testing.assert_array_equal(shared, one)
