@@ -191,6 +191,93 @@ def prefix_encode(cfg, tables, tensors, stream, reps: int = 5) -> dict:
             "plain_path_tokens_per_request": int(sum(len(x) for x in seqs))}
 
 
+def grouped_attention(cfg, n_req: int, stream, reps: int = 10) -> dict:
+    """R requests of the workload's shape (seeds 1000 + workload + 100 r), each with its own
+    prefix, in one blink_prefix_tail_attention_grouped launch, against R single launches."""
+    import torch
+
+    import pass_typed_decision_amd as blink
+    import synth
+
+    parts = ("q", "k_tail", "v_tail", "k_prefix", "v_prefix")
+    tails, offs, tens, pre_k, pre_v = [], [], {k: [] for k in parts[:3]}, [], []
+    base = 0
+    flops = 0.0
+    singles = []
+    for r in range(n_req):
+        rng = synth.rng_for(cfg, seed=1000 + cfg.number + 100 * r)
+        tables = synth.draw_tables(cfg, rng)
+        pk = blink.pack_ragged(tables.tail_len, cfg.prefix_len, cfg.token_budget, cfg.max_rows)
+        host = synth.draw_tensors(cfg, rng, pk.total_padded_tokens, parts)
+        tails.append(tables.tail_len)
+        offs.append(pk.token_offset + base)
+        base += pk.total_padded_tokens
+        for k in parts[:3]:
+            tens[k].append(host[k])
+        if cfg.prefix_len:
+            pre_k.append(host["k_prefix"])
+            pre_v.append(host["v_prefix"])
+        flops += attention_flops(cfg, tables.tail_len)
+        singles.append((tables.tail_len, pk, host))
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    tail_len = np.concatenate(tails).astype(np.int32)
+    vs = np.concatenate([[0], np.cumsum(tail_len)]).astype(np.int32)
+    q, kt, vt = (dev(np.concatenate(tens[k])) for k in parts[:3])
+    kp = dev(np.concatenate(pre_k)) if pre_k else None
+    vp = dev(np.concatenate(pre_v)) if pre_v else None
+    out = torch.empty_like(q)
+    first = np.concatenate([[0], np.cumsum([len(t) for t in tails])]).astype(np.int32)
+    plen = np.full(n_req, cfg.prefix_len, np.int32)
+    pstart = (np.arange(n_req) * cfg.prefix_len).astype(np.int64)
+    ga = blink.GroupedAttention(q, kt, vt, kp, vp, out,
+                                torch.as_tensor(np.concatenate(offs).astype(np.int64)).cuda(),
+                                torch.as_tensor(vs).cuda(), vs, first, pstart, plen, cfg.scale,
+                                stream=stream.cuda_stream)
+    # One request at a time, each its own launch over its own buffers.
+    lib = blink.load_library()
+    single_args = []
+    keep = []
+    for tl, pk, host in singles:
+        t = {k: dev(host[k]) for k in parts if host[k].size}
+        o = torch.empty_like(t["q"])
+        d_off = torch.as_tensor(pk.token_offset.astype(np.int64)).cuda()
+        d_vs = torch.as_tensor(pk.valid_start).cuda()
+        keep.append((t, o, d_off, d_vs))
+        single_args.append(blink.prefix_tail_attention(
+            t["q"], t["k_tail"], t["v_tail"], t.get("k_prefix"), t.get("v_prefix"), o, d_off,
+            d_vs, pk.total_valid_tokens, cfg.scale, stream=stream.cuda_stream, launch=False))
+
+    def run_singles():
+        for a in single_args:
+            if lib.blink_prefix_tail_attention(*a) != 0:
+                raise RuntimeError(lib.blink_last_error().decode())
+
+    ev = TimingEvents(4 * reps, stream)
+    ga.launch()
+    run_singles()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev.record(4 * i)
+        ga.launch()
+        ev.record(4 * i + 1)
+        ev.record(4 * i + 2)
+        run_singles()
+        ev.record(4 * i + 3)
+    torch.cuda.synchronize()
+    g_ms = float(np.mean([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(reps)]))
+    s_ms = float(np.mean([ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(reps)]))
+    ev.close()
+    return {"requests": n_req, "questions": int(len(tail_len)), "attention_ms": g_ms,
+            "tflops": flops / (g_ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "one_launch_per_request_ms": s_ms, "speedup": s_ms / g_ms,
+            "work_per_launch": f"{flops:.4e} FLOP"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +286,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--group", type=int, default=0, metavar="R",
+                    help="also time R requests of the workload's shape, each with its own "
+                         "prefix, in one grouped attention launch")
     ap.add_argument("--readout", default="per_option", choices=("per_option", "batched"),
                     help="readout form: per option (default), or batched over the distinct "
                          "label rows")
@@ -296,6 +386,7 @@ def main():
                 "work_per_launch": f"{abytes:.4e} B"}
 
     prefix = prefix_encode(cfg, tables, tensors, stream) if cfg.prefix_len > 0 else None
+    grouped = grouped_attention(cfg, args.group, stream) if args.group > 1 else None
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -345,6 +436,7 @@ def main():
             "label_pack_host_ms_once_per_request": label_pack_ms,
         },
         "prefix_encode_once_per_request": prefix,
+        "grouped_requests": grouped,
         "cpu_baseline": baseline,
     }
     print(json.dumps(line), flush=True)

@@ -49,6 +49,7 @@ extern "C" {
 #define BLINK_MAX_OPTIONS 255
 #define BLINK_MAX_INPUT_TOKENS 131072
 #define BLINK_TOKEN_BUDGET 32768
+#define BLINK_MAX_REQUESTS 64 /* prefixes in one grouped attention launch */
 #define BLINK_PREFIX_MIN_TOKENS 256 /* shared prefixes shorter than this take the plain path */
 
 /* Message for the calling thread's last failed call; "" after a successful call. */
@@ -56,7 +57,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 4
+#define BLINK_ABI_VERSION 5
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -188,6 +189,36 @@ int blink_prefix_tail_attention(const void *q, const void *k_tail, const void *v
                                 int64_t total_padded_tokens, int32_t prefix_len,
                                 int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
                                 float scale, void *stream);
+
+/*
+ * blink_prefix_tail_attention_grouped -- device, asynchronous.
+ *
+ * Several requests, each with its own shared prefix, in one launch (the cross-request group
+ * of the "public entry point" section: the questions of several requests share the forwards
+ * of one call). Every question attends to its own request's prefix exactly as in
+ * blink_prefix_tail_attention; results are bitwise those of one blink_prefix_tail_attention
+ * call per request. The requests' questions are laid out one request after another.
+ *
+ *   q, k_tail, v_tail, out, d_token_offset, d_valid_start: as in blink_prefix_tail_attention,
+ *                     over the questions of every request (1..512 questions in total)
+ *   h_valid_start[n+1]  host copy of d_valid_start (sizes the launch; must match it)
+ *   n_requests        1..64 (BLINK_MAX_REQUESTS; else BLINK_E_LIMIT)
+ *   h_request_first[n_requests+1]  host: first question of each request; [0] = 0,
+ *                     [n_requests] = n_questions, every request at least one question
+ *   h_prefix_start[n_requests]     host: first row of the request's prefix in k/v_prefix
+ *   h_prefix_len[n_requests]       host: the request's prefix length P_r >= 0
+ *                     (P_r + tail <= 131072 for each of its questions, else BLINK_E_LIMIT)
+ *   k_prefix, v_prefix  bf16 [total_prefix_rows, H_kv, D] device: every request's prefix
+ *                     K/V (requests may share rows); NULL iff total_prefix_rows == 0
+ *   n_heads_q, n_heads_kv, head_dim, scale: as in blink_prefix_tail_attention
+ */
+int blink_prefix_tail_attention_grouped(
+    const void *q, const void *k_tail, const void *v_tail, const void *k_prefix,
+    const void *v_prefix, void *out, const int64_t *d_token_offset, const int32_t *d_valid_start,
+    const int32_t *h_valid_start, int32_t n_questions, int64_t total_valid_tokens,
+    int64_t total_padded_tokens, int32_t n_requests, const int32_t *h_request_first,
+    const int64_t *h_prefix_start, const int32_t *h_prefix_len, int64_t total_prefix_rows,
+    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, float scale, void *stream);
 
 /*
  * blink_label_readout -- device, asynchronous.

@@ -23,7 +23,9 @@ from ._binding import (
     MAX_OPTIONS,
     MAX_QUESTIONS,
     TOKEN_BUDGET,
+    GroupedAttention,
     LabelRows,
+    MAX_REQUESTS,
     Pack,
     PREFIX_MIN_TOKENS,
     PrefixPlan,
@@ -55,7 +57,9 @@ __all__ = [
     "MAX_OPTIONS",
     "MAX_QUESTIONS",
     "TOKEN_BUDGET",
+    "GroupedAttention",
     "LabelRows",
+    "MAX_REQUESTS",
     "Pack",
     "PREFIX_MIN_TOKENS",
     "PrefixPlan",

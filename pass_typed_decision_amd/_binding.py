@@ -25,6 +25,7 @@ MAX_OPTIONS = 255
 MAX_INPUT_TOKENS = 131072
 TOKEN_BUDGET = 32768
 PREFIX_MIN_TOKENS = 256
+MAX_REQUESTS = 64
 
 # Every symbol declared in include/blink.h.
 EXPORTS = (
@@ -37,6 +38,7 @@ EXPORTS = (
     "blink_label_readout_batched",
     "blink_plan_prefix",
     "blink_assemble_answers",
+    "blink_prefix_tail_attention_grouped",
 )
 
 
@@ -97,6 +99,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.blink_assemble_answers.argtypes = [
         ctypes.POINTER(ctypes.c_float), _PI32, _PI32, _I32, _PI32,
         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.blink_prefix_tail_attention_grouped.restype = ctypes.c_int
+    lib.blink_prefix_tail_attention_grouped.argtypes = [
+        _P, _P, _P, _P, _P, _P, _P, _P, _PI32, _I32, _I64, _I64, _I32, _PI32, _PI64, _PI32, _I64,
+        _I32, _I32, _I32, _F32, _P,
+    ]
     lib.blink_plan_prefix.restype = ctypes.c_int
     lib.blink_plan_prefix.argtypes = [_PI32, _PI64, _I32, _I32, _PI32, _PI32, _PI64]
     _lib = lib
@@ -276,7 +283,8 @@ def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offs
     """Launches blink_prefix_tail_attention. Shapes: q/out [T_pad, H_q, D], k/v_tail
     [T_pad, H_kv, D], k/v_prefix [P, H_kv, D] or None; token_offset int64 [n],
     valid_start int32 [n + 1] (device). With ``launch=False`` returns the checked argument
-    list instead (index 9 is total_valid_tokens) for repeated launches."""
+    list instead (index 9 is total_valid_tokens) for repeated launches; it holds raw
+    addresses, so the caller keeps every tensor alive while the list is in use."""
     import torch
 
     bf = torch.bfloat16
@@ -307,6 +315,58 @@ def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offs
     if not launch:
         return args
     _check(lib.blink_prefix_tail_attention(*args))
+
+
+class GroupedAttention:
+    """Prepared launch of blink_prefix_tail_attention_grouped: several requests, each with
+    its own prefix, in one launch. q/out [T_pad, H_q, D], k/v_tail [T_pad, H_kv, D],
+    k/v_prefix [total prefix rows, H_kv, D] or None (device, bf16); token_offset int64 [n] and
+    valid_start int32 [n + 1] on the device, with valid_start's host copy; request_first
+    int32 [R + 1], prefix_start int64 [R], prefix_len int32 [R] on the host. The object holds
+    every tensor and host array it was given, since ``launch()`` passes their addresses again
+    on each call."""
+
+    def __init__(self, q, k_tail, v_tail, k_prefix, v_prefix, out, token_offset, valid_start,
+                 h_valid_start, request_first, prefix_start, prefix_len, scale: float,
+                 stream=None):
+        import torch
+
+        bf = torch.bfloat16
+        t_pad, hq, d = q.shape
+        hkv = k_tail.shape[1]
+        if tuple(k_tail.shape) != (t_pad, hkv, d) or tuple(v_tail.shape) != (t_pad, hkv, d):
+            raise BlinkError(BLINK_E_INVALID, "k_tail/v_tail must be [T_pad, H_kv, D]")
+        if tuple(out.shape) != (t_pad, hq, d):
+            raise BlinkError(BLINK_E_INVALID, "out must be [T_pad, H_q, D]")
+        rows = 0 if k_prefix is None else int(k_prefix.shape[0])
+        if rows:
+            if tuple(k_prefix.shape) != (rows, hkv, d) or tuple(v_prefix.shape) != (rows, hkv, d):
+                raise BlinkError(BLINK_E_INVALID, "k_prefix/v_prefix must be [rows, H_kv, D]")
+            kp, vp = _dev(k_prefix, bf, "k_prefix"), _dev(v_prefix, bf, "v_prefix")
+        else:
+            kp = vp = ctypes.c_void_p(0)
+        self.h_vs = np.ascontiguousarray(np.asarray(h_valid_start, np.int32))
+        self.first = np.ascontiguousarray(np.asarray(request_first, np.int32))
+        self.pstart = np.ascontiguousarray(np.asarray(prefix_start, np.int64))
+        self.plen = np.ascontiguousarray(np.asarray(prefix_len, np.int32))
+        n = int(token_offset.shape[0])
+        n_req = int(self.first.shape[0]) - 1
+        if self.h_vs.shape[0] != n + 1 or int(valid_start.shape[0]) != n + 1:
+            raise BlinkError(BLINK_E_INVALID, "valid_start must have n + 1 entries")
+        if n_req < 0 or self.pstart.shape[0] != n_req or self.plen.shape[0] != n_req:
+            raise BlinkError(BLINK_E_INVALID, "request tables must have R + 1, R and R entries")
+        self._tensors = (q, k_tail, v_tail, k_prefix, v_prefix, out, token_offset, valid_start)
+        self.lib = load_library()
+        self.args = [
+            _dev(q, bf, "q"), _dev(k_tail, bf, "k_tail"), _dev(v_tail, bf, "v_tail"), kp, vp,
+            _dev(out, bf, "out"), _dev(token_offset, torch.int64, "token_offset"),
+            _dev(valid_start, torch.int32, "valid_start"), _ptr(self.h_vs, ctypes.c_int32), n,
+            int(self.h_vs[-1]), int(t_pad), n_req, _ptr(self.first, ctypes.c_int32),
+            _ptr(self.pstart, ctypes.c_int64), _ptr(self.plen, ctypes.c_int32), rows, int(hq),
+            int(hkv), int(d), float(scale), _stream(stream)]
+
+    def launch(self):
+        _check(self.lib.blink_prefix_tail_attention_grouped(*self.args))
 
 
 def encode_prefix_attention(q, k, v, out, scale: float, stream=None):
@@ -340,7 +400,8 @@ def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature: float,
     w_u [vocab, d_model] bf16, cand_ids int32 [sum K], cand_off int32 [n + 1];
     outputs logits float32 [sum K] (device), probs float32 [sum K] and argmax int32 [n] (device,
     or pinned host memory, readable once the stream is synchronised). With ``launch=False``
-    returns the checked argument list instead, for repeated launches."""
+    returns the checked argument list instead, for repeated launches; it holds raw addresses,
+    so the caller keeps every tensor alive while the list is in use."""
     import torch
 
     bf = torch.bfloat16
@@ -406,7 +467,8 @@ def label_readout_batched(hidden, last_row, w_u, cand_off, row_id, row_first, ro
     """Launches blink_label_readout_batched: as label_readout, with the option table given
     by its CSR offsets and its distinct-row tables (row_id int32 [U], row_first int32 [U + 1],
     row_entry int32 [sum K], device; from pack_labels). With ``launch=False`` returns the
-    checked argument list instead, for repeated launches."""
+    checked argument list instead, for repeated launches; it holds raw addresses, so the
+    caller keeps every tensor alive while the list is in use."""
     import torch
 
     bf = torch.bfloat16

@@ -95,6 +95,7 @@ constexpr int kRowsPerUnit = kWaves * kRowsPerWave;  // 384
 constexpr int kTileKeys = 64;
 constexpr int kStages = 4;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxRequests = BLINK_MAX_REQUESTS;  // prefixes in one grouped launch
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
 constexpr float kSumLimit = 0x1p64f;            // 2^kHeadroom: largest row sum a pass accepts
@@ -113,7 +114,7 @@ struct Args {
   int n;
   int64_t total_valid;
   int64_t t_pad;
-  int prefix_len;
+  int64_t prefix_rows;  // rows of the prefix K/V buffers (every request's prefix)
   int hq;
   int hkv;
   int group;
@@ -121,6 +122,15 @@ struct Args {
   int64_t full_units;  // per KV head: units [0, full_units) hold kRowsPerUnit rows each,
   int small_rows;      // later units small_rows each (see unit_split)
   int64_t n_units;     // per KV head
+  // Requests of the launch: 1 for blink_prefix_tail_attention (units as above). A grouped
+  // launch gives each request its own units (no unit spans two requests, so each unit has
+  // exactly one prefix): request r holds questions [req_first[r], req_first[r+1]), units
+  // [req_unit[r], req_unit[r+1]) and prefix rows [req_pstart[r], req_pstart[r] + req_plen[r]).
+  int n_req;
+  int req_first[kMaxRequests + 1];
+  int64_t req_unit[kMaxRequests + 1];
+  int64_t req_pstart[kMaxRequests];
+  int req_plen[kMaxRequests];
 };
 
 template <int D>
@@ -253,7 +263,7 @@ struct TileRsrc {
 template <int D>
 __device__ inline TileRsrc tile_rsrc(const Args &a, int g, const TileSrc &s) {
   const bool pre = s.q < 0;
-  const int64_t rowcount = pre ? int64_t(a.prefix_len) : a.t_pad;  // rows that exist
+  const int64_t rowcount = pre ? a.prefix_rows : a.t_pad;  // rows that exist
   const int64_t row0 = s.rowbase + s.kstart;
   const int64_t stride = int64_t(a.hkv) * D;  // elements between consecutive rows
   int64_t nkeys = min(int64_t(kTileKeys), int64_t(s.klimit - s.kstart));
@@ -480,6 +490,8 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
 
 struct Unit {
   int qa, qz, posz;  // questions touched by the workgroup; last row's position in qz
+  int plen;          // the unit's prefix: rows [pstart, pstart + plen) of the prefix K/V
+  int64_t pstart;
 };
 
 __device__ inline TileSrc tail_from(const Args &a, const Tables &tab, const Unit &u, int q) {
@@ -502,11 +514,11 @@ __device__ inline TileSrc tail_from(const Args &a, const Tables &tab, const Unit
 }
 
 __device__ inline TileSrc first_tile(const Args &a, const Tables &tab, const Unit &u) {
-  if (a.prefix_len > 0) {
+  if (u.plen > 0) {
     TileSrc s{};
-    s.rowbase = 0;
+    s.rowbase = u.pstart;
     s.kstart = 0;
-    s.klimit = a.prefix_len;
+    s.klimit = u.plen;
     s.q = -1;
     s.valid = true;
     return s;
@@ -592,7 +604,7 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) fresh |= rs[qb].m == -INFINITY;
     // A whole tile: every key visible to every row of the wave (see the two tile paths).
-    const bool whole = cur.q < 0 ? cur.kstart + kTileKeys <= a.prefix_len
+    const bool whole = cur.q < 0 ? cur.kstart + kTileKeys <= cur.klimit
                                  : cur.q == ws.qa && ws.qa == ws.qz &&
                                        cur.kstart + kTileKeys <= ws.posa + 1;
     const bool fast = !max_only && whole && !__builtin_amdgcn_ballot_w64(fresh);
@@ -611,13 +623,13 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int base = cur.kstart + 32 * sub;  // first key of the sub-tile
-        const bool masked = !(cur.q < 0 && base + 32 <= a.prefix_len);
+        const bool masked = !(cur.q < 0 && base + 32 <= cur.klimit);
         int lim[kQB];
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           int last;  // last visible key of this row, relative to the sub-tile start
           if (cur.q < 0)
-            last = a.prefix_len - 1 - base;
+            last = cur.klimit - 1 - base;  // a prefix tile's klimit is the prefix length
           else
             last = (rt.rq[qb] == cur.q) ? rt.rpos[qb] - base : -1;
           last = min(last, 31);
@@ -750,15 +762,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   __syncthreads();
   const int64_t valid_total = min(int64_t(uniform(sm.tab.start[a.n])), a.total_valid);
   const int64_t R = valid_total * G;
-  const int64_t row0 = unit < a.full_units
-                           ? unit * kRowsPerUnit
-                           : a.full_units * kRowsPerUnit + (unit - a.full_units) * a.small_rows;
-  if (row0 >= R) return;  // uniform across the workgroup
-  const int64_t row_end =
-      min(R, row0 + (unit < a.full_units ? int64_t(kRowsPerUnit) : int64_t(a.small_rows)));
+  Unit u;
+  int64_t row0, row_end;
+  if (a.n_req == 1) {
+    row0 = unit < a.full_units ? unit * kRowsPerUnit
+                               : a.full_units * kRowsPerUnit + (unit - a.full_units) * a.small_rows;
+    row_end = row0 + (unit < a.full_units ? int64_t(kRowsPerUnit) : int64_t(a.small_rows));
+    u.plen = a.req_plen[0];
+    u.pstart = a.req_pstart[0];
+  } else {
+    int r = 0;  // the unit's request: the last r with req_unit[r] <= unit
+    while (r + 1 < a.n_req && a.req_unit[r + 1] <= unit) ++r;
+    const int64_t rows_end = int64_t(uniform(sm.tab.start[a.req_first[r + 1]])) * G;
+    row0 = int64_t(uniform(sm.tab.start[a.req_first[r]])) * G +
+           (unit - a.req_unit[r]) * kRowsPerUnit;
+    row_end = min(rows_end, row0 + kRowsPerUnit);
+    u.plen = a.req_plen[r];
+    u.pstart = a.req_pstart[r];
+  }
+  row_end = min(R, row_end);
+  if (row0 < 0 || row0 >= row_end) return;  // uniform across the workgroup
 
   // Questions touched by the workgroup and by this wave.
-  Unit u;
   {
     const int64_t c0 = row0 / G, cz = (row_end - 1) / G;
     u.qa = uniform(find_question(sm.tab.start, a.n, c0));
@@ -880,12 +905,92 @@ inline int64_t unit_split(int64_t rows, int hkv, int cus, int64_t &full_units, i
 
 template <int D>
 hipError_t launch(const Args &a, hipStream_t stream) {
-  const int64_t blocks =
-      (a.full_units + (a.total_valid * a.group - a.full_units * kRowsPerUnit + a.small_rows - 1) /
-                          a.small_rows) * a.hkv;
+  const int64_t blocks = a.n_units * a.hkv;  // exactly n_units units per KV head
   hipLaunchKernelGGL(prefix_tail_attention_kernel<D>, dim3(unsigned(blocks)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+namespace {
+
+struct Shape {
+  int32_t n_questions;
+  int64_t total_valid_tokens, total_padded_tokens;
+  int32_t n_heads_q, n_heads_kv, head_dim;
+  float scale;
+};
+
+// Checks shared by both entry points; returns BLINK_OK or the failing status.
+int check_shape(const void *q, const void *k_tail, const void *v_tail, const void *out,
+                const int64_t *d_token_offset, const int32_t *d_valid_start, const Shape &sh) {
+  using blink::fail;
+  if (sh.n_questions < 1 || sh.n_questions > BLINK_MAX_QUESTIONS)
+    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", sh.n_questions,
+                BLINK_MAX_QUESTIONS);
+  if (!q || !k_tail || !v_tail || !out || !d_token_offset || !d_valid_start)
+    return fail(BLINK_E_INVALID, "prefix tail attention: a pointer argument is NULL");
+  if (sh.head_dim != 64 && sh.head_dim != 128)
+    return fail(BLINK_E_INVALID, "head_dim %d is not supported (64 or 128)", sh.head_dim);
+  if (sh.n_heads_kv < 1 || sh.n_heads_q < sh.n_heads_kv || sh.n_heads_q % sh.n_heads_kv ||
+      sh.n_heads_q / sh.n_heads_kv > kMaxGroup)
+    return fail(BLINK_E_INVALID, "head counts %d/%d: need H_q a multiple of H_kv, group <= %d",
+                sh.n_heads_q, sh.n_heads_kv, kMaxGroup);
+  // A 64-key tile's byte span from its first row must fit a 32-bit buffer offset.
+  if (int64_t(kTileKeys) * sh.n_heads_kv * sh.head_dim * 2 >= (int64_t(1) << 31))
+    return fail(BLINK_E_LIMIT, "%d KV heads of %d dims are too wide for one tile", sh.n_heads_kv,
+                sh.head_dim);
+  if (!(sh.scale > 0.f) || !isfinite(sh.scale))
+    return fail(BLINK_E_INVALID, "scale must be finite and positive");
+  if (sh.total_valid_tokens < sh.n_questions ||
+      sh.total_padded_tokens < sh.total_valid_tokens ||
+      sh.total_valid_tokens > int64_t(sh.n_questions) * BLINK_MAX_INPUT_TOKENS)
+    return fail(BLINK_E_INVALID, "token totals do not fit: %lld real of %lld padded for %d "
+                "questions", (long long)sh.total_valid_tokens, (long long)sh.total_padded_tokens,
+                sh.n_questions);
+  return BLINK_OK;
+}
+
+int run(Args &a, const void *q, const void *k_tail, const void *v_tail, const void *k_prefix,
+        const void *v_prefix, void *out, const int64_t *d_token_offset,
+        const int32_t *d_valid_start, const Shape &sh, void *stream) {
+  using blink::fail;
+  const void *ptrs[] = {q, k_tail, v_tail, out, a.prefix_rows ? k_prefix : q,
+                        a.prefix_rows ? v_prefix : q};
+  for (const void *p : ptrs)
+    if (!blink::aligned16(p)) return fail(BLINK_E_INVALID, "tensors must be 16-byte aligned");
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_tail = static_cast<const uint16_t *>(k_tail);
+  a.v_tail = static_cast<const uint16_t *>(v_tail);
+  a.k_pre = static_cast<const uint16_t *>(k_prefix);
+  a.v_pre = static_cast<const uint16_t *>(v_prefix);
+  a.out = static_cast<uint16_t *>(out);
+  a.token_offset = d_token_offset;
+  a.valid_start = d_valid_start;
+  a.n = sh.n_questions;
+  a.total_valid = sh.total_valid_tokens;
+  a.t_pad = sh.total_padded_tokens;
+  a.hq = sh.n_heads_q;
+  a.hkv = sh.n_heads_kv;
+  a.group = sh.n_heads_q / sh.n_heads_kv;
+  a.scale_log2 = sh.scale * kLog2e;
+  if (a.n_units * a.hkv > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "launch too large");
+  (void)hipGetLastError();
+  const hipError_t err = sh.head_dim == 64 ? launch<64>(a, static_cast<hipStream_t>(stream))
+                                           : launch<128>(a, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(BLINK_E_DEVICE, "prefix tail attention launch: %s", hipGetErrorString(err));
+  return blink::ok();
+}
+
+int device_cus(int &cus) {
+  int device = 0;
+  cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return blink::fail(BLINK_E_DEVICE, "prefix tail attention: no device");
+  return BLINK_OK;
 }
 
 }  // namespace
@@ -899,71 +1004,91 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
                                            int32_t n_heads_q, int32_t n_heads_kv,
                                            int32_t head_dim, float scale, void *stream) {
   using blink::fail;
-  if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
-  if (!q || !k_tail || !v_tail || !out || !d_token_offset || !d_valid_start)
-    return fail(BLINK_E_INVALID, "blink_prefix_tail_attention: a pointer argument is NULL");
+  const Shape sh{n_questions, total_valid_tokens, total_padded_tokens, n_heads_q, n_heads_kv,
+                 head_dim, scale};
+  int rc = check_shape(q, k_tail, v_tail, out, d_token_offset, d_valid_start, sh);
+  if (rc != BLINK_OK) return rc;
   if (prefix_len < 0 || prefix_len >= BLINK_MAX_INPUT_TOKENS)
     return fail(BLINK_E_LIMIT, "prefix of %d tokens leaves no room under the maximum context "
                 "length of %d", prefix_len, BLINK_MAX_INPUT_TOKENS);
   if (prefix_len > 0 && (!k_prefix || !v_prefix))
     return fail(BLINK_E_INVALID, "prefix K/V pointers are NULL with prefix_len %d", prefix_len);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(BLINK_E_INVALID, "head_dim %d is not supported (64 or 128)", head_dim);
-  if (n_heads_kv < 1 || n_heads_q < n_heads_kv || n_heads_q % n_heads_kv ||
-      n_heads_q / n_heads_kv > kMaxGroup)
-    return fail(BLINK_E_INVALID, "head counts %d/%d: need H_q a multiple of H_kv, group <= %d",
-                n_heads_q, n_heads_kv, kMaxGroup);
-  // A 64-key tile's byte span from its first row must fit a 32-bit buffer offset.
-  if (int64_t(kTileKeys) * n_heads_kv * head_dim * 2 >= (int64_t(1) << 31))
-    return fail(BLINK_E_LIMIT, "%d KV heads of %d dims are too wide for one tile", n_heads_kv,
-                head_dim);
-  if (!(scale > 0.f) || !isfinite(scale))
-    return fail(BLINK_E_INVALID, "scale must be finite and positive");
-  if (total_valid_tokens < n_questions || total_padded_tokens < total_valid_tokens ||
-      total_valid_tokens > int64_t(n_questions) * BLINK_MAX_INPUT_TOKENS)
-    return fail(BLINK_E_INVALID, "token totals do not fit: %lld real of %lld padded for %d "
-                "questions", (long long)total_valid_tokens, (long long)total_padded_tokens,
-                n_questions);
-  int device = 0, cus = 0;
-  if (hipGetDevice(&device) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-    return fail(BLINK_E_DEVICE, "blink_prefix_tail_attention: no device");
-  int64_t full_units = 0;
-  int small_rows = 0;
-  const int64_t units = unit_split(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv,
-                                   cus, full_units, small_rows);
-  if (units * n_heads_kv > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "launch too large");
-  const void *ptrs[] = {q, k_tail, v_tail, out, prefix_len ? k_prefix : q,
-                        prefix_len ? v_prefix : q};
-  for (const void *p : ptrs)
-    if (!blink::aligned16(p)) return fail(BLINK_E_INVALID, "tensors must be 16-byte aligned");
+  int cus = 0;
+  if ((rc = device_cus(cus)) != BLINK_OK) return rc;
+  Args a{};
+  a.n_units = unit_split(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv, cus,
+                         a.full_units, a.small_rows);
+  a.prefix_rows = prefix_len;
+  a.n_req = 1;
+  a.req_first[0] = 0;
+  a.req_first[1] = n_questions;
+  a.req_unit[0] = 0;
+  a.req_unit[1] = a.n_units;
+  a.req_pstart[0] = 0;
+  a.req_plen[0] = prefix_len;
+  return run(a, q, k_tail, v_tail, k_prefix, v_prefix, out, d_token_offset, d_valid_start, sh,
+             stream);
+}
 
-  Args a;
-  a.q = static_cast<const uint16_t *>(q);
-  a.k_tail = static_cast<const uint16_t *>(k_tail);
-  a.v_tail = static_cast<const uint16_t *>(v_tail);
-  a.k_pre = static_cast<const uint16_t *>(k_prefix);
-  a.v_pre = static_cast<const uint16_t *>(v_prefix);
-  a.out = static_cast<uint16_t *>(out);
-  a.token_offset = d_token_offset;
-  a.valid_start = d_valid_start;
-  a.n = n_questions;
-  a.total_valid = total_valid_tokens;
-  a.t_pad = total_padded_tokens;
-  a.prefix_len = prefix_len;
-  a.hq = n_heads_q;
-  a.hkv = n_heads_kv;
-  a.group = n_heads_q / n_heads_kv;
-  a.scale_log2 = scale * kLog2e;
-  a.full_units = full_units;
-  a.small_rows = small_rows;
+extern "C" int blink_prefix_tail_attention_grouped(
+    const void *q, const void *k_tail, const void *v_tail, const void *k_prefix,
+    const void *v_prefix, void *out, const int64_t *d_token_offset, const int32_t *d_valid_start,
+    const int32_t *h_valid_start, int32_t n_questions, int64_t total_valid_tokens,
+    int64_t total_padded_tokens, int32_t n_requests, const int32_t *h_request_first,
+    const int64_t *h_prefix_start, const int32_t *h_prefix_len, int64_t total_prefix_rows,
+    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, float scale, void *stream) {
+  using blink::fail;
+  const Shape sh{n_questions, total_valid_tokens, total_padded_tokens, n_heads_q, n_heads_kv,
+                 head_dim, scale};
+  int rc = check_shape(q, k_tail, v_tail, out, d_token_offset, d_valid_start, sh);
+  if (rc != BLINK_OK) return rc;
+  if (n_requests < 1 || n_requests > kMaxRequests)
+    return fail(BLINK_E_LIMIT, "%d requests; supported 1-%d", n_requests, kMaxRequests);
+  if (!h_valid_start || !h_request_first || !h_prefix_start || !h_prefix_len)
+    return fail(BLINK_E_INVALID, "prefix tail attention: a pointer argument is NULL");
+  if (total_prefix_rows < 0 || (total_prefix_rows > 0 && (!k_prefix || !v_prefix)))
+    return fail(BLINK_E_INVALID, "prefix K/V pointers are NULL with %lld prefix rows",
+                (long long)total_prefix_rows);
+  if (h_valid_start[0] != 0 || h_valid_start[n_questions] != total_valid_tokens)
+    return fail(BLINK_E_INVALID, "valid_start must run from 0 to total_valid_tokens");
+  for (int i = 0; i < n_questions; ++i)
+    if (h_valid_start[i + 1] <= h_valid_start[i])
+      return fail(BLINK_E_INVALID, "question %d has an empty tail", i);
+  if (h_request_first[0] != 0 || h_request_first[n_requests] != n_questions)
+    return fail(BLINK_E_INVALID, "request_first must run from 0 to n_questions");
+  const int G = n_heads_q / n_heads_kv;
+  Args a{};
+  a.prefix_rows = total_prefix_rows;
+  a.n_req = n_requests;
+  a.full_units = 0;
+  a.small_rows = kRowsPerUnit;
+  int64_t units = 0;
+  for (int r = 0; r < n_requests; ++r) {
+    const int f = h_request_first[r], l = h_request_first[r + 1];
+    if (l <= f) return fail(BLINK_E_INVALID, "request %d has no questions", r);
+    const int64_t ps = h_prefix_start[r];
+    const int pl = h_prefix_len[r];
+    if (pl < 0 || ps < 0 || ps + pl > total_prefix_rows)
+      return fail(BLINK_E_INVALID, "request %d: prefix rows [%lld, %lld) outside the %lld "
+                  "prefix rows", r, (long long)ps, (long long)(ps + pl),
+                  (long long)total_prefix_rows);
+    for (int i = f; i < l; ++i) {
+      const int64_t total = int64_t(pl) + (h_valid_start[i + 1] - h_valid_start[i]);
+      if (total > BLINK_MAX_INPUT_TOKENS)
+        return fail(BLINK_E_LIMIT, "question %d renders to %lld tokens, over the maximum "
+                    "context length of %d", i, (long long)total, BLINK_MAX_INPUT_TOKENS);
+    }
+    a.req_first[r] = f;
+    a.req_unit[r] = units;
+    a.req_pstart[r] = ps;
+    a.req_plen[r] = pl;
+    const int64_t rows = int64_t(h_valid_start[l] - h_valid_start[f]) * G;
+    units += (rows + kRowsPerUnit - 1) / kRowsPerUnit;
+  }
+  a.req_first[n_requests] = n_questions;
+  a.req_unit[n_requests] = units;
   a.n_units = units;
-
-  (void)hipGetLastError();
-  const hipError_t err = head_dim == 64 ? launch<64>(a, static_cast<hipStream_t>(stream))
-                                        : launch<128>(a, static_cast<hipStream_t>(stream));
-  if (err != hipSuccess)
-    return fail(BLINK_E_DEVICE, "blink_prefix_tail_attention launch: %s", hipGetErrorString(err));
-  return blink::ok();
+  a.full_units = units;
+  return run(a, q, k_tail, v_tail, k_prefix, v_prefix, out, d_token_offset, d_valid_start, sh,
+             stream);
 }

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 4
+    assert blink.load_library().blink_abi_version() == 5
 
 
 def _compare(pk, ref):
@@ -361,3 +361,43 @@ def test_assemble_answers_refusals(blink, probs, off, types, code, msg):
     with pytest.raises(blink.BlinkError) as e:
         blink.assemble_answers(probs, off, types)
     assert e.value.code == code and msg in str(e.value)
+
+
+def _grouped(lib, n=3, total=9, t_pad=12, vs=(0, 3, 5, 9), first=(0, 2, 3), pstart=(0, 4),
+             plen=(4, 2), rows=6, hq=4, hkv=1, d=64):
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    h_vs = np.asarray(vs, np.int32)
+    fi = np.asarray(first, np.int32)
+    ps = np.asarray(pstart, np.int64)
+    pl = np.asarray(plen, np.int32)
+    n_req = len(first) - 1
+    return lib.blink_prefix_tail_attention_grouped(
+        fake, fake, fake, fake if rows else None, fake if rows else None, fake, fake, fake,
+        _ptr32(h_vs), n, total, t_pad, n_req, _ptr32(fi),
+        ps.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr32(pl), rows, hq, hkv, d, 0.125,
+        None)
+
+
+def _ptr32(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+@pytest.mark.parametrize("kw, code, msg", [
+    (dict(first=(0,), pstart=(), plen=()), -2, "0 requests; supported 1-64"),
+    (dict(first=tuple(range(66)), pstart=(0,) * 65, plen=(0,) * 65, n=65, total=65, t_pad=65,
+          vs=tuple(range(66))), -2, "65 requests; supported 1-64"),
+    (dict(first=(0, 2, 2)), -1, "request_first must run from 0 to n_questions"),
+    (dict(first=(0, 3, 3)), -1, "request 1 has no questions"),
+    (dict(first=(0, 0, 3)), -1, "request 0 has no questions"),
+    (dict(pstart=(0, 5)), -1, "request 1: prefix rows [5, 7) outside the 6 prefix rows"),
+    (dict(plen=(4, -1)), -1, "request 1: prefix rows"),
+    (dict(vs=(0, 3, 3, 9)), -1, "question 1 has an empty tail"),
+    (dict(vs=(0, 3, 5, 8)), -1, "valid_start must run from 0 to total_valid_tokens"),
+    (dict(rows=0), -1, "prefix rows"),
+    (dict(plen=(4, 131070), rows=131080, pstart=(0, 4)), -2,
+     "question 2 renders to 131074 tokens, over the maximum context length of 131072"),
+])
+def test_grouped_attention_refusals_before_launch(blink, kw, code, msg):
+    lib = blink.load_library()
+    assert _grouped(lib, **kw) == code
+    assert msg in lib.blink_last_error().decode()
