@@ -22,6 +22,10 @@ HIP_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    # The kernels' bodies are compiled in the device pass only, so the host pass sees their
+    # helpers unused.
+    "-Wno-unused-function",
+    "-Wno-unneeded-internal-declaration",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # Matrix-core results in VGPRs: the attention softmax reads its score accumulators with
     # ordinary vector instructions, and the Q fragments it pins in AGPRs feed MFMAs directly.

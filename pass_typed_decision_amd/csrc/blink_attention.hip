@@ -99,6 +99,7 @@ constexpr int kMaxRequests = BLINK_MAX_REQUESTS;  // prefixes in one grouped lau
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
 constexpr float kSumLimit = 0x1p64f;            // 2^kHeadroom: largest row sum a pass accepts
+static_assert(kSumLimit == 0x1p64f && kHeadroom == 64.0f, "the row-sum check is 2^kHeadroom");
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3 (32-bit data)
 constexpr int kWaitFlags = 0xF70;               // s_waitcnt with expcnt/lgkmcnt at their max
 
