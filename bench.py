@@ -35,7 +35,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
 # counted on; a changed kernel reports null until it is counted again.
 MEASURED_TRAFFIC = {
-    2: ("893d1a3d2cc4651e1336a079ec1d5ce5c2d8e9d0204ab31c07ae895d8a45ef4c", 123755911),
+    2: ("56200d4d877c65fe968062ca26e485f98749c27b4861d6ffd7d5841defba7cbf", 124062577),
 }
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 

@@ -158,3 +158,24 @@ def test_prepared_launch_holds_its_tables():
     del clutter
     got = bf16_to_f32_host(out)
     _check_bitwise_against_single(group, got, range(len(cfgs)))
+
+
+def test_sixty_four_requests_of_512_questions():
+    # The largest group: 64 requests (the whole request table) with 512 questions in all,
+    # prefixes of 0..190 tokens (some within one tile, some several), short tails.
+    cfgs = [synth.config(2, n_heads_q=8, n_heads_kv=2, prefix_len=(r * 37) % 191,
+                         n_questions=8, tail_lo=1, tail_hi=40) for r in range(64)]
+    print("grouped attention: 64 requests, 512 questions", flush=True)
+    group = Group(cfgs, [500 + r for r in range(64)])
+    assert len(group.tail_len) == 512
+    got = group.run()
+    ref = attention_grouped(group.tensors["q"], group.tensors["k_tail"], group.tensors["v_tail"],
+                            group.k_prefix, group.v_prefix, group.token_offset, group.tail_len,
+                            group.request_first, group.prefix_start, group.prefix_len, group.hq,
+                            group.hkv, group.scale)
+    rows = np.concatenate([np.arange(o, o + n) for o, n in zip(group.token_offset,
+                                                                group.tail_len)])
+    err = np.abs(got[rows] - ref[rows]).max()
+    print(f"  max abs err {err:.3e} over {rows.size} rows", flush=True)
+    assert np.isfinite(got[rows]).all() and err <= ATTN_TOL
+    _check_bitwise_against_single(group, got, [0, 31, 63])
