@@ -20,7 +20,10 @@ It follows the blink.py page (thegovind/blink-4b):
                      computed ("torch engine" section: _shared_prefix_len, _prefill_tokens,
                      _forward; PREFIX_MIN_TOKENS in "constants the deployment sets");
   * ``answers``   -- typed answers from the option probabilities ("answer assembly" section:
-                     answer_for).
+                     answer_for);
+  * ``scoring``   -- teacher-forced scoring of a sequence's last tokens: full-vocabulary
+                     log-softmax at each scored row, read at the next token (the simit MoT
+                     engine page: score_len).
 
 Arithmetic is float64 throughout; bf16 inputs are widened exactly.
 Every function is pinned by tests under ``tests/test_oracle_*.py``; none is "parity unpinned".
@@ -38,6 +41,7 @@ from .readout import label_readout, label_readout_batched, label_rows, softmax_t
 from .path import score_request
 from .prefix import plan_prefix, shared_prefix_len, PREFIX_MIN_TOKENS
 from .answers import answer_for, assemble
+from .scoring import score_rows, teacher_forced_logprobs
 
 __all__ = [
     "pack_ragged",
@@ -60,4 +64,6 @@ __all__ = [
     "PREFIX_MIN_TOKENS",
     "answer_for",
     "assemble",
+    "score_rows",
+    "teacher_forced_logprobs",
 ]
