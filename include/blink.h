@@ -19,7 +19,8 @@
  *  - Every argument error is detected before anything is launched; a call that fails
  *    validation has no effect on device memory.
  *  - The caller owns all memory and the stream. The library allocates no device memory,
- *    keeps no global state between calls and may be called from several threads.
+ *    keeps no global state between calls and may be called from several threads. The one
+ *    call that needs scratch memory (blink_score_targets) takes it from the caller.
  *  - Device entry points are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream). Device arrays must stay alive until the work on `stream` has finished.
  *  - bf16 means the 16-bit brain-float storage format. All tensors are dense and row-major
@@ -57,7 +58,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 5
+#define BLINK_ABI_VERSION 6
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -310,6 +311,33 @@ int blink_label_readout_batched(const void *hidden, int64_t hidden_rows, int32_t
 int blink_assemble_answers(const float *probs, const int32_t *cand_off, const int32_t *qtype,
                            int32_t n_questions, int32_t *choice, double *confidence,
                            double *value);
+
+/*
+ * blink_score_targets -- device, asynchronous.
+ *
+ * Teacher-forced scoring (the simit MoT engine page: score_len and its logits consumer): for
+ * scored row j, h = hidden[rows[j]]; z_v = sum_d W_U[v, d] * h[d] over the whole vocabulary
+ * (bf16 products, FP32 accumulation, bf16 matrix cores); logprob[j] = z_{targets[j]} -
+ * log(sum_v exp(z_v)). A sequence of n tokens scored on its last S tokens uses the rows at
+ * positions n - S - 1 .. n - 2, each with the next position's token as its target.
+ *
+ *   hidden      bf16 [hidden_rows, d_model] device; d_model a multiple of 64, 64..16384
+ *   d_rows      int64 [n_rows] device: hidden row of each scored row
+ *   d_targets   int32 [n_rows] device: target token of each scored row
+ *   n_rows      1..2^20
+ *   w_u         bf16 [vocab, d_model] device, vocab 1..2^31
+ *   d_logprob   float32 [n_rows] device output; NaN for a row whose index or target is out
+ *               of range
+ *   workspace   device scratch of at least blink_score_targets_workspace(n_rows, vocab)
+ *               bytes, 16-byte aligned; owned by the caller, its contents are not preserved
+ *               (else BLINK_E_INVALID)
+ * Calls that share one workspace on different streams race.
+ */
+size_t blink_score_targets_workspace(int32_t n_rows, int64_t vocab); /* 0 for bad sizes */
+int blink_score_targets(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                        const int64_t *d_rows, const int32_t *d_targets, int32_t n_rows,
+                        const void *w_u, int64_t vocab, float *d_logprob, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ from ._binding import (
     Pack,
     PREFIX_MIN_TOKENS,
     PrefixPlan,
+    TargetScorer,
     ANSWER_CHOICE,
     ANSWER_NOUL,
     ANSWER_SCORE,
@@ -63,6 +64,7 @@ __all__ = [
     "Pack",
     "PREFIX_MIN_TOKENS",
     "PrefixPlan",
+    "TargetScorer",
     "plan_prefix",
     "ANSWER_CHOICE",
     "ANSWER_NOUL",

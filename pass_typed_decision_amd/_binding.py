@@ -39,6 +39,8 @@ EXPORTS = (
     "blink_plan_prefix",
     "blink_assemble_answers",
     "blink_prefix_tail_attention_grouped",
+    "blink_score_targets_workspace",
+    "blink_score_targets",
 )
 
 
@@ -104,6 +106,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         _P, _P, _P, _P, _P, _P, _P, _P, _PI32, _I32, _I64, _I64, _I32, _PI32, _PI64, _PI32, _I64,
         _I32, _I32, _I32, _F32, _P,
     ]
+    lib.blink_score_targets_workspace.restype = ctypes.c_size_t
+    lib.blink_score_targets_workspace.argtypes = [_I32, _I64]
+    lib.blink_score_targets.restype = ctypes.c_int
+    lib.blink_score_targets.argtypes = [_P, _I64, _I32, _P, _P, _I32, _P, _I64, _P, _P,
+                                        ctypes.c_size_t, _P]
     lib.blink_plan_prefix.restype = ctypes.c_int
     lib.blink_plan_prefix.argtypes = [_PI32, _PI64, _I32, _I32, _PI32, _PI32, _PI64]
     _lib = lib
@@ -367,6 +374,39 @@ class GroupedAttention:
 
     def launch(self):
         _check(self.lib.blink_prefix_tail_attention_grouped(*self.args))
+
+
+class TargetScorer:
+    """Prepared teacher-forced scoring (blink_score_targets): log p(target | row) over the full
+    vocabulary for n scored rows. hidden [T, d_model] and w_u [vocab, d_model] bf16, rows int64
+    [n] and targets int32 [n] (device). The workspace is allocated here, once; ``run()`` queues
+    the two kernels and returns the float32 [n] device tensor of log-probabilities."""
+
+    def __init__(self, hidden, w_u, rows, targets, stream=None):
+        import torch
+
+        bf = torch.bfloat16
+        if hidden.dim() != 2 or w_u.dim() != 2 or hidden.shape[1] != w_u.shape[1]:
+            raise BlinkError(BLINK_E_INVALID, "hidden and w_u must be 2-D with the same width")
+        n = int(rows.shape[0])
+        if int(targets.shape[0]) != n:
+            raise BlinkError(BLINK_E_INVALID, "rows and targets must have the same length")
+        self.lib = load_library()
+        size = int(self.lib.blink_score_targets_workspace(n, int(w_u.shape[0])))
+        if size == 0:
+            raise BlinkError(BLINK_E_INVALID, "no workspace size for these sizes")
+        self.workspace = torch.empty(size, dtype=torch.uint8, device=hidden.device)
+        self.logprob = torch.empty(n, dtype=torch.float32, device=hidden.device)
+        self._tensors = (hidden, w_u, rows, targets)
+        self.args = [
+            _dev(hidden, bf, "hidden"), int(hidden.shape[0]), int(hidden.shape[1]),
+            _dev(rows, torch.int64, "rows"), _dev(targets, torch.int32, "targets"), n,
+            _dev(w_u, bf, "w_u"), int(w_u.shape[0]), _dev(self.logprob, torch.float32, "logprob"),
+            ctypes.c_void_p(self.workspace.data_ptr()), size, _stream(stream)]
+
+    def run(self):
+        _check(self.lib.blink_score_targets(*self.args))
+        return self.logprob
 
 
 def encode_prefix_attention(q, k, v, out, scale: float, stream=None):

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libblink.so")
-SOURCES = ["blink_host.cpp", "blink_attention.hip", "blink_readout.hip"]
+SOURCES = ["blink_host.cpp", "blink_attention.hip", "blink_readout.hip", "blink_scoring.hip"]
 ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}",

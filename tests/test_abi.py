@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 5
+    assert blink.load_library().blink_abi_version() == 6
 
 
 def _compare(pk, ref):
@@ -400,4 +400,34 @@ def _ptr32(a):
 def test_grouped_attention_refusals_before_launch(blink, kw, code, msg):
     lib = blink.load_library()
     assert _grouped(lib, **kw) == code
+    assert msg in lib.blink_last_error().decode()
+
+
+def test_score_targets_workspace_size(blink):
+    lib = blink.load_library()
+    slices = (151936 + 127) // 128
+    need = lib.blink_score_targets_workspace(256, 151936)
+    assert need >= slices * 256 * 8 + 256 * 4 and need % 256 == 0
+    assert lib.blink_score_targets_workspace(0, 100) == 0
+    assert lib.blink_score_targets_workspace(5, 0) == 0
+
+
+def _score(lib, n=4, d_model=128, vocab=1000, ws=1 << 20, null=False, rows=10):
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    return lib.blink_score_targets(fake, rows, d_model, fake, fake, n, None if null else fake,
+                                   vocab, fake, fake, ws, None)
+
+
+@pytest.mark.parametrize("kw, code, msg", [
+    (dict(n=0), -2, "0 scored rows"),
+    (dict(d_model=100), -1, "d_model 100 must be a multiple of 64"),
+    (dict(d_model=32768), -1, "d_model 32768 must be a multiple of 64"),
+    (dict(vocab=0), -1, "vocab in 1..2^31"),
+    (dict(rows=0), -1, "hidden_rows must be positive"),
+    (dict(ws=100), -1, "workspace of 100 bytes; 512 needed"),
+    (dict(null=True), -1, "a pointer argument is NULL"),
+])
+def test_score_targets_refusals_before_launch(blink, kw, code, msg):
+    lib = blink.load_library()
+    assert _score(lib, **kw) == code
     assert msg in lib.blink_last_error().decode()
