@@ -278,6 +278,45 @@ def grouped_attention(cfg, n_req: int, stream, reps: int = 10) -> dict:
             "work_per_launch": f"{flops:.4e} FLOP"}
 
 
+def teacher_forced_scoring(cfg, tables, pk, tensors, stream, score_len: int = 8,
+                           reps: int = 10) -> dict:
+    """The request's questions scored teacher-forced on their last score_len tokens: the rows
+    n_i - score_len - 1 .. n_i - 2 of each tail (shorter tails give what they have), each
+    against a synthetic next token, log-softmax over the whole vocabulary (blink_score_targets)."""
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    rng = np.random.Generator(np.random.PCG64(4000 + cfg.number))
+    rows = []
+    for off, n in zip(pk.token_offset, tables.tail_len):
+        lo = max(0, int(n) - score_len - 1)
+        rows.extend(int(off) + i for i in range(lo, int(n) - 1))
+    targets = rng.integers(0, cfg.vocab, size=len(rows)).astype(np.int32)
+    sc = blink.TargetScorer(tensors["hidden"], tensors["w_u"],
+                            torch.as_tensor(np.asarray(rows, np.int64)).cuda(),
+                            torch.as_tensor(targets).cuda(), stream=stream.cuda_stream)
+    ev = TimingEvents(2 * reps, stream)
+    sc.run()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev.record(2 * i)
+        sc.run()
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
+    ev.close()
+    m = len(rows)
+    flops = 2.0 * m * cfg.vocab * cfg.d_model
+    wbytes = float(cfg.vocab) * cfg.d_model * 2 + m * cfg.d_model * 2
+    return {"rows": m, "score_len": score_len, "ms": ms,
+            "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "hbm_gbps": wbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "work_per_call": f"{flops:.4e} FLOP, {wbytes:.4e} B"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +426,7 @@ def main():
 
     prefix = prefix_encode(cfg, tables, tensors, stream) if cfg.prefix_len > 0 else None
     grouped = grouped_attention(cfg, args.group, stream) if args.group > 1 else None
+    scoring = teacher_forced_scoring(cfg, tables, pk, tensors, stream)
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -437,6 +477,7 @@ def main():
         },
         "prefix_encode_once_per_request": prefix,
         "grouped_requests": grouped,
+        "teacher_forced_scoring": scoring,
         "cpu_baseline": baseline,
     }
     print(json.dumps(line), flush=True)

@@ -405,9 +405,10 @@ def test_grouped_attention_refusals_before_launch(blink, kw, code, msg):
 
 def test_score_targets_workspace_size(blink):
     lib = blink.load_library()
-    slices = (151936 + 127) // 128
     need = lib.blink_score_targets_workspace(256, 151936)
-    assert need >= slices * 256 * 8 + 256 * 4 and need % 256 == 0
+    # (max, sum) per row and vocabulary slice, plus one target logit per row
+    assert need % 256 == 0 and need >= 256 * 4 + 256 * 8 * (151936 // 256)
+    assert lib.blink_score_targets_workspace(512, 151936) >= 2 * need - 512
     assert lib.blink_score_targets_workspace(0, 100) == 0
     assert lib.blink_score_targets_workspace(5, 0) == 0
 
