@@ -10,9 +10,9 @@
 // unembedding rows, M small (questions x score_len) and V = 151936, so W must be read from
 // HBM exactly once while H (M x d_model, a few MB) is re-read from L2:
 //  * score_partials_kernel: one workgroup per 128-row slice of the vocabulary and per block
-//    of up to 256 scored rows. Both operands go through LDS in chunks of 64 hidden elements
-//    (a 128 x 64 slice of W and a 256 x 64 slice of H, rows padded by 16 bytes), and each of
-//    the 8 waves computes Z^T for its 32 rows with v_mfma_f32_32x32x16_bf16 (4 vocabulary
+//    of up to 256 scored rows (128 for calls of at most 128 rows). Both operands go through LDS in chunks of 64 hidden elements
+//    (a 128 x 64 slice of W and a 256 x 64 slice of H, rows padded by 16 bytes), and each
+//    wave computes Z^T for its 32 rows with v_mfma_f32_32x32x16_bf16 (4 vocabulary
 //    tiles of 32). Computing Z^T puts one scored row per lane (and its partner lane l ^ 32),
 //    so the slice's maximum and sum of exp are lane-local but for one exchange. The slice
 //    writes (max, sum of exp(z - max)) per row to the workspace, and the logit of the row's
@@ -31,18 +31,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerBlock = 32 * kWaves;  // scored rows per workgroup
 constexpr int kVocabPerBlock = 128;         // vocabulary rows per workgroup: 4 tiles of 32
 constexpr int kChunk = 64;                  // hidden elements per LDS stage
 constexpr int kStride = kChunk * 2 + 16;    // LDS row stride in bytes
 constexpr int kMaxDModel = 16384;
 constexpr int64_t kMaxRows = int64_t(1) << 20;
 
+template <int ROWS>
 struct Smem {
   alignas(16) char w[kVocabPerBlock * kStride];
-  alignas(16) char h[kRowsPerBlock * kStride];
+  alignas(16) char h[ROWS * kStride];
 };
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -51,27 +49,34 @@ __device__ inline bool row_ok(int64_t idx, int64_t hidden_rows) {
   return idx >= 0 && idx < hidden_rows;
 }
 
-// Four waves per SIMD (at most 128 VGPRs): two workgroups share a CU, so one's chunk loads
-// overlap the other's matrix work.
-__global__ __launch_bounds__(kThreads, 4) void score_partials_kernel(
+// WAVES waves of 32 scored rows each. With 8 waves (256 rows) the kernel keeps four waves per
+// SIMD (at most 128 VGPRs), so two workgroups share a CU; with 4 waves (128 rows, for calls of
+// at most 128 rows) it keeps three per SIMD, so three workgroups share a CU. Either way one
+// workgroup's chunk loads overlap another's matrix work.
+template <int WAVES, int MIN_WAVES_PER_SIMD>
+__global__ __launch_bounds__(64 * WAVES, MIN_WAVES_PER_SIMD) void score_partials_kernel(
     const uint16_t *__restrict__ hidden, int64_t hidden_rows, int d_model,
     const int64_t *__restrict__ rows, const int32_t *__restrict__ targets, int n_rows,
     const uint16_t *__restrict__ w_u, int64_t vocab, float2 *__restrict__ part,
     float *__restrict__ target_z) {
-  __shared__ Smem sm;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kRowsPerBlock = 32 * WAVES;
+  constexpr int kWPieces = kVocabPerBlock * 8 / kThreads;  // W pieces per thread
+  constexpr int kRowStep = kThreads / 8;                    // rows one pass of pieces covers
+  __shared__ Smem<kRowsPerBlock> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int64_t v0 = int64_t(blockIdx.x) * kVocabPerBlock;
   const int m0 = int(blockIdx.y) * kRowsPerBlock;
 
-  // Staging: 16-byte pieces, 8 per row of a chunk. W: 1024 pieces (2 per thread); H: 2048
-  // pieces (4 per thread). A thread keeps the same rows for every chunk.
+  // Staging: 16-byte pieces, 8 per row of a chunk: 1024 W pieces (kWPieces per thread) and
+  // 8 * kRowsPerBlock H pieces (4 per thread). A thread keeps the same rows for every chunk.
   const int piece_col = tid & 7;
-  const uint16_t *wsrc[2];
-  bool wvalid[2];
+  const uint16_t *wsrc[kWPieces];
+  bool wvalid[kWPieces];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (tid >> 3) + 64 * i;
+  for (int i = 0; i < kWPieces; ++i) {
+    const int r = (tid >> 3) + kRowStep * i;
     wvalid[i] = v0 + r < vocab;
     wsrc[i] = w_u + (wvalid[i] ? (v0 + r) * int64_t(d_model) : 0) + piece_col * 8;
   }
@@ -79,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 4) void score_partials_kernel(
   bool hvalid[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 64 * i;
+    const int r = (tid >> 3) + kRowStep * i;
     const int m = m0 + r;
     const int64_t idx = m < n_rows ? rows[m] : -1;
     hvalid[i] = row_ok(idx, hidden_rows);
@@ -95,10 +100,10 @@ __global__ __launch_bounds__(kThreads, 4) void score_partials_kernel(
 
   // The next chunk's global loads are issued before the current chunk's matrix work, so
   // their latency overlaps it; they land in LDS after the second barrier.
-  u32x4 wreg[2], hreg[4];
+  u32x4 wreg[kWPieces], hreg[4];
   auto fetch = [&](int kc) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kWPieces; ++i) {
       wreg[i] = u32x4{0u, 0u, 0u, 0u};
       if (wvalid[i])
         wreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wsrc[i] + kc));
@@ -112,12 +117,12 @@ __global__ __launch_bounds__(kThreads, 4) void score_partials_kernel(
   fetch(0);
   for (int kc = 0; kc < d_model; kc += kChunk) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4 *>(sm.w + ((tid >> 3) + 64 * i) * kStride + piece_col * 16) =
+    for (int i = 0; i < kWPieces; ++i)
+      *reinterpret_cast<u32x4 *>(sm.w + ((tid >> 3) + kRowStep * i) * kStride + piece_col * 16) =
           wreg[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(sm.h + ((tid >> 3) + 64 * i) * kStride + piece_col * 16) =
+      *reinterpret_cast<u32x4 *>(sm.h + ((tid >> 3) + kRowStep * i) * kStride + piece_col * 16) =
           hreg[i];
     __syncthreads();
     if (kc + kChunk < d_model) fetch(kc + kChunk);
@@ -240,11 +245,16 @@ extern "C" int blink_score_targets(const void *hidden, int64_t hidden_rows, int3
   float *target_z = reinterpret_cast<float *>(static_cast<char *>(workspace) + part_bytes);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const dim3 grid(unsigned(slices), unsigned((n_rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL(score_partials_kernel, grid, dim3(kThreads), 0, s,
-                     static_cast<const uint16_t *>(hidden), hidden_rows, d_model, d_rows,
-                     d_targets, n_rows, static_cast<const uint16_t *>(w_u), vocab, part,
-                     target_z);
+  const uint16_t *h = static_cast<const uint16_t *>(hidden);
+  const uint16_t *w = static_cast<const uint16_t *>(w_u);
+  if (n_rows <= 128) {  // one block of 4 waves per slice: three workgroups per CU
+    hipLaunchKernelGGL((score_partials_kernel<4, 3>), dim3(unsigned(slices)), dim3(256), 0, s, h,
+                       hidden_rows, d_model, d_rows, d_targets, n_rows, w, vocab, part, target_z);
+  } else {  // blocks of 256 rows: W is read once for every 256 scored rows
+    const dim3 grid(unsigned(slices), unsigned((n_rows + 255) / 256));
+    hipLaunchKernelGGL((score_partials_kernel<8, 4>), grid, dim3(512), 0, s, h, hidden_rows,
+                       d_model, d_rows, d_targets, n_rows, w, vocab, part, target_z);
+  }
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) {
     hipLaunchKernelGGL(score_finish_kernel, dim3(unsigned((n_rows + 3) / 4)), dim3(256), 0, s,
