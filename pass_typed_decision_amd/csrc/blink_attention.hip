@@ -885,17 +885,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
 // CU at a time. Uniform units of kRowsPerUnit rows leave the last round of workgroups partly
 // empty, yet it lasts a full unit's time. Instead the rows left after the full rounds are
 // spread over every CU of the last round, in units whose waves give each SIMD fewer waves
-// (multiples of 4 waves), so that round ends sooner. Returns the units per head.
+// (multiples of 4 waves), so that round ends sooner; a launch of less than one round is cut
+// the same way from the start. Returns the units per head.
 inline int64_t unit_split(int64_t rows, int hkv, int cus, int64_t &full_units, int &small_rows) {
   const int64_t units = (rows + kRowsPerUnit - 1) / kRowsPerUnit;
   full_units = units;
   small_rows = kRowsPerUnit;
   const int64_t per_round = cus / hkv;  // units of one head in one round
-  if (per_round < 1 || units * hkv <= cus) return units;
+  const int64_t simd_rows = 4 * kRowsPerWave;  // one wave on each SIMD
+  if (per_round < 1) return units;
+  if (units * hkv <= cus) {
+    // Less than one round: cut the rows into smaller units so that they cover every CU.
+    const int64_t want = (rows + per_round - 1) / per_round;
+    const int64_t up = max(simd_rows, (want + simd_rows - 1) / simd_rows * simd_rows);
+    if (up >= kRowsPerUnit) return units;
+    full_units = 0;
+    small_rows = int(up);
+    return (rows + up - 1) / up;
+  }
   const int64_t full = units / per_round * per_round;
   const int64_t rem = rows - full * kRowsPerUnit;
   if (rem <= 0) return units;
-  const int64_t simd_rows = 4 * kRowsPerWave;  // one wave on each SIMD
   const int64_t small = (rem + per_round - 1) / per_round;
   const int64_t small_up = (small + simd_rows - 1) / simd_rows * simd_rows;
   if (small_up >= kRowsPerUnit) return units;
