@@ -35,7 +35,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
 # counted on; a changed kernel reports null until it is counted again.
 MEASURED_TRAFFIC = {
-    2: ("56200d4d877c65fe968062ca26e485f98749c27b4861d6ffd7d5841defba7cbf", 124062577),
+    2: ("c4bbd623c741cf3a409163b2b7d3199900586d058de0f2f7528facacebb4d7db", 124026902),
 }
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 
