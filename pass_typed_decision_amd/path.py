@@ -39,6 +39,13 @@ _LABELS = list(string.ascii_uppercase) + [
 _HIP_MEMCPY_H2D = 1
 
 
+def _hip_runtime():
+    try:
+        return ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+    except OSError as exc:
+        raise RuntimeError("the HIP runtime is not loaded in this process") from exc
+
+
 def _hip_memcpy_async():
     """hipMemcpyAsync of the HIP runtime this process already runs (torch and libblink.so
     share one copy). Queuing a copy through it avoids torch's stream-context switch, which
@@ -69,6 +76,11 @@ class ScoringStep:
     argmax straight into one pinned host buffer. Those host buffers are reused, so a step
     queued with ``run(fetch=False)`` must be synchronised before the next step is packed.
 
+    ``depth`` (1 or 2) is the number of steps that may be in flight: with 2, the host buffers
+    (pinned row tables and results) are doubled, so step k + 1 can be packed and queued with
+    ``submit()`` while step k still runs; ``collect()`` waits for the oldest step and returns its
+    results. Device buffers are shared: the stream runs the steps' kernels in order.
+
     ``readout``: "per_option" (blink_label_readout, the default) or "batched"
     (blink_label_readout_batched over the request's distinct label rows, built once here by
     blink_pack_labels). Both give bitwise the same results; on MI355X the per-option form is
@@ -77,12 +89,14 @@ class ScoringStep:
     def __init__(self, tail_len, cand_ids, cand_off, tensors: dict, n_heads_q: int,
                  n_heads_kv: int, prefix_len: int, temperature: float, scale: float,
                  token_budget: int = TOKEN_BUDGET, max_rows: int = 0, stream=None,
-                 readout: str = "per_option"):
+                 readout: str = "per_option", depth: int = 1):
         import ctypes
 
         import torch
 
         self.torch = torch
+        if depth not in (1, 2):
+            raise BlinkError(BLINK_E_INVALID, "depth must be 1 or 2")
         self.tail_len = np.ascontiguousarray(np.asarray(tail_len, np.int32))
         n = self.n = int(self.tail_len.shape[0])
         self.prefix_len = int(prefix_len)
@@ -168,6 +182,43 @@ class ScoringStep:
                 self.temperature, self.max_options, self.logits, self.h_probs, self.h_argmax,
                 stream=self.stream.cuda_stream, launch=False)
 
+        # Slot 0 is the buffers above; a second slot doubles the host-side ones.
+        hip = _hip_runtime()
+        self._ev_record, self._ev_sync = hip.hipEventRecord, hip.hipEventSynchronize
+        self._ev_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._ev_sync.argtypes = [ctypes.c_void_p]
+        self._stream_handle = stream_handle
+        self._slots = [self._slot(hip, self.h_tab, self.h_res, self._pack_args, self._up_args,
+                                  self._read_args)]
+        for _ in range(depth - 1):
+            h_tab = torch.zeros_like(self.h_tab, pin_memory=True)
+            h_res = torch.empty_like(self.h_res, pin_memory=True)
+            tab = h_tab.numpy()
+            pack_args = pack_ragged_args(
+                self.tail_len, self.prefix_len, self.token_budget, self.max_rows, self._order,
+                self._batch_of, self._row_of, tab[:n], tab[n:2 * n],
+                tab[2 * n:].view(np.int32)[:n + 1], self._batch_first, self._batch_width,
+                self._batch_base, self._nb, self._tp, self._tv)
+            up_args = (self._up_args[0], ctypes.c_void_p(h_tab.data_ptr())) + self._up_args[2:]
+            read_args = list(self._read_args)
+            # the last three pointers before the stream are logits, probs and argmax
+            read_args[-3] = ctypes.c_void_p(h_res.data_ptr())
+            read_args[-2] = ctypes.c_void_p(h_res[total:].data_ptr())
+            self._slots.append(self._slot(hip, h_tab, h_res, pack_args, up_args, read_args))
+        self._next = 0
+        self._queue = []
+
+    def _slot(self, hip, h_tab, h_res, pack_args, up_args, read_args):
+        from types import SimpleNamespace
+
+        ev = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        total = int(self.logits.shape[0])
+        return SimpleNamespace(h_tab=h_tab, h_res=h_res, pack_args=pack_args, up_args=up_args,
+                               read_args=read_args, event=ev, busy=False,
+                               probs=h_res[:total], argmax=h_res[total:].view(self.torch.int32))
+
     @staticmethod
     def _call(fn, args):
         rc = fn(*args)
@@ -209,3 +260,35 @@ class ScoringStep:
             return None
         self.stream.synchronize()
         return self.h_probs.numpy(), self.h_argmax.numpy()
+
+    def submit(self):
+        """Packs the next step into a free slot and queues it (upload, attention, readout and
+        a completion event). At most ``depth`` steps may be outstanding."""
+        slot = self._slots[self._next]
+        if slot.busy:
+            raise BlinkError(BLINK_E_INVALID, "every slot holds a step that was not collected")
+        self._call(self._pack_fn, slot.pack_args)
+        if self._tp.value != self.pack.total_padded_tokens:
+            raise BlinkError(BLINK_E_INVALID, "tensors were not laid out for this pack")
+        self._copy(slot.up_args)
+        self.attention(self._tv.value)
+        self._call(self._read_fn, slot.read_args)
+        if self._ev_record(slot.event, self._stream_handle) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        slot.busy = True
+        self._queue.append(slot)
+        self._next = (self._next + 1) % len(self._slots)
+
+    def outstanding(self) -> int:
+        return len(self._queue)
+
+    def collect(self):
+        """Waits for the oldest submitted step; returns its (probs, argmax) host arrays, valid
+        until that slot is submitted again."""
+        if not self._queue:
+            raise BlinkError(BLINK_E_INVALID, "no step to collect")
+        slot = self._queue.pop(0)
+        if self._ev_sync(slot.event) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        slot.busy = False
+        return slot.probs.numpy(), slot.argmax.numpy()

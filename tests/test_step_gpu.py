@@ -90,3 +90,40 @@ def test_typed_answers_from_the_step():
         q = np.sort(p[off[i]:off[i + 1]])
         if len(q) == 1 or q[-1] - q[-2] > 1e-5:
             assert choice[i] == c
+
+
+def test_pipelined_steps_match_oracle():
+    # Two steps in flight (double host buffers): every collected step must carry its own
+    # complete results, checked against the oracle, with the result buffers poisoned first.
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(1)
+    req = Request(cfg)
+    ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
+    step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows, depth=2)
+    z, p, a = label_readout(req.tensors["hidden"], req.pack["last_row"], req.tensors["w_u"],
+                            req.tables.cand_ids, req.tables.cand_off, cfg.temperature)
+    for slot in step._slots:
+        slot.h_res.fill_(float("nan"))
+    torch.cuda.synchronize()
+    seen = 0
+    for i in range(7):
+        step.submit()
+        if step.outstanding() == 2:
+            probs, arg = step.collect()
+            assert float(np.abs(probs - p).max()) <= PROB_TOL
+            check_argmax(z, req.tables.cand_off, a, arg)
+            probs[:] = np.nan  # the slot must be rewritten by its next step
+            seen += 1
+    with pytest.raises(blink.BlinkError):
+        step.submit()
+        step.submit()  # a third outstanding step has no free slot
+    while step.outstanding():
+        probs, arg = step.collect()
+        assert float(np.abs(probs - p).max()) <= PROB_TOL
+        seen += 1
+    assert seen == 8  # 7 + 1 submitted, all collected
