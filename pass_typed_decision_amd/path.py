@@ -76,10 +76,12 @@ class ScoringStep:
     argmax straight into one pinned host buffer. Those host buffers are reused, so a step
     queued with ``run(fetch=False)`` must be synchronised before the next step is packed.
 
-    ``depth`` (1 or 2) is the number of steps that may be in flight: with 2, the host buffers
-    (pinned row tables and results) are doubled, so step k + 1 can be packed and queued with
-    ``submit()`` while step k still runs; ``collect()`` waits for the oldest step and returns its
-    results. Device buffers are shared: the stream runs the steps' kernels in order.
+    ``depth`` (1 or 2) is the number of steps that may be in flight. With 2, a second slot has
+    its own pinned row tables and results, its own device row tables, attention output and
+    logits, and its own stream (default priority), so step k + 1 can be packed and queued with
+    ``submit()`` while step k still runs, and its kernels can start on compute units that
+    step k's last workgroups leave idle; ``collect()`` waits for the oldest step and returns its
+    results. The request's inputs are shared and only read.
 
     ``readout``: "per_option" (blink_label_readout, the default) or "batched"
     (blink_label_readout_batched over the request's distinct label rows, built once here by
@@ -190,21 +192,46 @@ class ScoringStep:
         self._stream_handle = stream_handle
         self._slots = [self._slot(hip, self.h_tab, self.h_res, self._pack_args, self._up_args,
                                   self._read_args)]
+        self._slots[0].stream, self._slots[0].stream_handle = self.stream, stream_handle
+        self._slots[0].attn_args = self._attn_args
         for _ in range(depth - 1):
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(self.stream)  # the request's inputs, queued on the main stream
+            side_handle = ctypes.c_void_p(side.cuda_stream)
             h_tab = torch.zeros_like(self.h_tab, pin_memory=True)
             h_res = torch.empty_like(self.h_res, pin_memory=True)
+            d_tab = torch.zeros_like(self.d_tab)
+            out = torch.empty_like(self.out)
+            logits = torch.empty_like(self.logits)
             tab = h_tab.numpy()
             pack_args = pack_ragged_args(
                 self.tail_len, self.prefix_len, self.token_budget, self.max_rows, self._order,
                 self._batch_of, self._row_of, tab[:n], tab[n:2 * n],
                 tab[2 * n:].view(np.int32)[:n + 1], self._batch_first, self._batch_width,
                 self._batch_base, self._nb, self._tp, self._tv)
-            up_args = (self._up_args[0], ctypes.c_void_p(h_tab.data_ptr())) + self._up_args[2:]
-            read_args = list(self._read_args)
-            # the last three pointers before the stream are logits, probs and argmax
-            read_args[-3] = ctypes.c_void_p(h_res.data_ptr())
-            read_args[-2] = ctypes.c_void_p(h_res[total:].data_ptr())
-            self._slots.append(self._slot(hip, h_tab, h_res, pack_args, up_args, read_args))
+            up_args = (ctypes.c_void_p(d_tab.data_ptr()), ctypes.c_void_p(h_tab.data_ptr()),
+                       self._up_args[2], _HIP_MEMCPY_H2D, side_handle)
+            d_off, d_last = d_tab[:n], d_tab[n:2 * n]
+            d_vs = d_tab[2 * n:].view(torch.int32)[:n + 1]
+            attn_args = prefix_tail_attention(
+                t["q"], t["k_tail"], t["v_tail"], t.get("k_prefix"), t.get("v_prefix"), out,
+                d_off, d_vs, pk.total_valid_tokens, self.scale, stream=side.cuda_stream,
+                launch=False)
+            probs, argmax = h_res[:total], h_res[total:].view(torch.int32)
+            if readout == "batched":
+                read_args = label_readout_batched(
+                    t["hidden"], d_last, t["w_u"], self.cand_off, *self.d_rows,
+                    self.temperature, self.max_options, logits, probs, argmax,
+                    stream=side.cuda_stream, launch=False)
+            else:
+                read_args = label_readout(
+                    t["hidden"], d_last, t["w_u"], self.cand_ids, self.cand_off,
+                    self.temperature, self.max_options, logits, probs, argmax,
+                    stream=side.cuda_stream, launch=False)
+            slot = self._slot(hip, h_tab, h_res, pack_args, up_args, read_args)
+            slot.stream, slot.stream_handle, slot.attn_args = side, side_handle, attn_args
+            slot.keep = (d_tab, out, logits)  # the argument lists hold their raw addresses
+            self._slots.append(slot)
         self._next = 0
         self._queue = []
 
@@ -271,9 +298,10 @@ class ScoringStep:
         if self._tp.value != self.pack.total_padded_tokens:
             raise BlinkError(BLINK_E_INVALID, "tensors were not laid out for this pack")
         self._copy(slot.up_args)
-        self.attention(self._tv.value)
+        slot.attn_args[9] = int(self._tv.value)
+        self._call(self._attn_fn, slot.attn_args)
         self._call(self._read_fn, slot.read_args)
-        if self._ev_record(slot.event, self._stream_handle) != 0:
+        if self._ev_record(slot.event, slot.stream_handle) != 0:
             raise RuntimeError("hipEventRecord failed")
         slot.busy = True
         self._queue.append(slot)

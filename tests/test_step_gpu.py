@@ -127,3 +127,43 @@ def test_pipelined_steps_match_oracle():
         assert float(np.abs(probs - p).max()) <= PROB_TOL
         seen += 1
     assert seen == 8  # 7 + 1 submitted, all collected
+
+
+def test_pipelined_full_size_is_bitwise_sequential():
+    # The 4B-like request two steps deep, the second slot on its own stream, so consecutive
+    # steps' kernels overlap on the GPU: every collected result and both slots' attention
+    # outputs must equal a synchronised step's bit for bit.
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(2)
+    req = Request(cfg)
+    ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
+    step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows, depth=2)
+    probs0, arg0 = (x.copy() for x in step.run())
+    out0 = step.out.clone()
+    rows = torch.as_tensor(valid_rows(req)).cuda()
+    for slot in step._slots:
+        slot.h_res.fill_(float("nan"))
+    step._slots[1].keep[1].fill_(float("nan"))
+    step.out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    collected = 0
+    for i in range(6):
+        step.submit()
+        if step.outstanding() == 2:
+            probs, arg = step.collect()
+            assert np.array_equal(probs, probs0) and np.array_equal(arg, arg0)
+            collected += 1
+    while step.outstanding():
+        probs, arg = step.collect()
+        assert np.array_equal(probs, probs0) and np.array_equal(arg, arg0)
+        collected += 1
+    torch.cuda.synchronize()
+    assert collected == 6
+    for out in (step.out, step._slots[1].keep[1]):
+        assert torch.equal(out[rows].view(torch.int16), out0[rows].view(torch.int16))
+    print("  six overlapped steps bitwise equal to a synchronised one", flush=True)
