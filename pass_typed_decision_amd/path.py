@@ -235,6 +235,23 @@ class ScoringStep:
         self._next = 0
         self._queue = []
 
+    def close(self):
+        """Waits for outstanding steps and releases the slots' completion events."""
+        while getattr(self, "_queue", None):
+            self.collect()
+        hip = _hip_runtime()
+        for slot in getattr(self, "_slots", []):
+            if slot.event:
+                hip.hipEventDestroy(slot.event)
+                slot.event = None
+        self._slots = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown: the runtime may already be gone
+            pass
+
     def _slot(self, hip, h_tab, h_res, pack_args, up_args, read_args):
         from types import SimpleNamespace
 
@@ -291,6 +308,8 @@ class ScoringStep:
     def submit(self):
         """Packs the next step into a free slot and queues it (upload, attention, readout and
         a completion event). At most ``depth`` steps may be outstanding."""
+        if not self._slots:
+            raise BlinkError(BLINK_E_INVALID, "the step was closed")
         slot = self._slots[self._next]
         if slot.busy:
             raise BlinkError(BLINK_E_INVALID, "every slot holds a step that was not collected")

@@ -127,6 +127,11 @@ def test_pipelined_steps_match_oracle():
         assert float(np.abs(probs - p).max()) <= PROB_TOL
         seen += 1
     assert seen == 8  # 7 + 1 submitted, all collected
+    step.submit()
+    step.close()  # waits for the outstanding step, then releases the events
+    assert step.outstanding() == 0
+    with pytest.raises(blink.BlinkError, match="closed"):
+        step.submit()
 
 
 def test_pipelined_full_size_is_bitwise_sequential():
