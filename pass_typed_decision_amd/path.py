@@ -184,7 +184,8 @@ class ScoringStep:
                 self.temperature, self.max_options, self.logits, self.h_probs, self.h_argmax,
                 stream=self.stream.cuda_stream, launch=False)
 
-        # Slot 0 is the buffers above; a second slot doubles the host-side ones.
+        # Slot 0 is the buffers above, on the caller's stream. A second slot gets its own host
+        # and device buffers and its own stream (see the class docstring).
         hip = _hip_runtime()
         self._ev_record, self._ev_sync = hip.hipEventRecord, hip.hipEventSynchronize
         self._ev_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
