@@ -92,9 +92,10 @@ def test_typed_answers_from_the_step():
             assert choice[i] == c
 
 
-def test_pipelined_steps_match_oracle():
-    # Two steps in flight (double host buffers): every collected step must carry its own
-    # complete results, checked against the oracle, with the result buffers poisoned first.
+@pytest.mark.parametrize("readout", ["per_option", "batched"])
+def test_pipelined_steps_match_oracle(readout):
+    # Two steps in flight (the second slot on its own stream): every collected step must carry
+    # its own complete results, checked against the oracle, with the result buffers poisoned.
     import torch
 
     import pass_typed_decision_amd as blink
@@ -104,7 +105,8 @@ def test_pipelined_steps_match_oracle():
     ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
     step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
                              cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
-                             cfg.scale, cfg.token_budget, cfg.max_rows, depth=2)
+                             cfg.scale, cfg.token_budget, cfg.max_rows, depth=2,
+                             readout=readout)
     z, p, a = label_readout(req.tensors["hidden"], req.pack["last_row"], req.tensors["w_u"],
                             req.tables.cand_ids, req.tables.cand_off, cfg.temperature)
     for slot in step._slots:
