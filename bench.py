@@ -319,6 +319,40 @@ def teacher_forced_scoring(cfg, tables, pk, tensors, stream, score_len: int = 8,
             "work_per_call": f"{flops:.4e} FLOP, {wbytes:.4e} B"}
 
 
+def library_references(stream, reps: int = 10) -> dict:
+    """What the vendor libraries reach on this device, measured beside the vendor peaks: a
+    large square bf16 matrix product (torch.matmul, i.e. hipBLASLt) and a 1 GiB streaming read
+    (torch's sum over the buffer). They are practical reference points, not peaks: this path's
+    kernels can exceed them."""
+    import torch
+
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    buf = torch.ones(1 << 28, device="cuda", dtype=torch.float32)  # 1 GiB
+    ev = TimingEvents(4 * reps, stream)
+    torch.matmul(a, b)
+    buf.sum()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev.record(4 * i)
+        torch.matmul(a, b)
+        ev.record(4 * i + 1)
+        ev.record(4 * i + 2)
+        buf.sum()
+        ev.record(4 * i + 3)
+    torch.cuda.synchronize()
+    gemm_ms = float(np.median([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(reps)]))
+    read_ms = float(np.median([ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(reps)]))
+    ev.close()
+    del a, b, buf
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_tflops": 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12,
+            "hbm_read_gbps": float(1 << 30) / (read_ms * 1e-3) / 1e9,
+            "what": "torch.matmul 8192^3 bf16; sum over a 1 GiB float32 buffer; medians of "
+                    f"{reps}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,6 +482,10 @@ def main():
     grouped = grouped_attention(cfg, args.group, stream) if args.group > 1 else None
     scoring = teacher_forced_scoring(cfg, tables, pk, tensors, stream)
 
+    refs = library_references(stream)
+    roof["frac_of_library_reference"] = roof["achieved"] / (
+        refs["bf16_gemm_tflops"] if roof["bound"] == "mfma" else refs["hbm_read_gbps"])
+
     baseline = None
     if not args.no_cpu_baseline:
         baseline = cpu_baseline(cfg, tables, host, args.cpu_budget)
@@ -502,6 +540,7 @@ def main():
         "prefix_encode_once_per_request": prefix,
         "grouped_requests": grouped,
         "teacher_forced_scoring": scoring,
+        "library_references": refs,
         "cpu_baseline": baseline,
     }
     print(json.dumps(line), flush=True)
