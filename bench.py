@@ -361,6 +361,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--depth", type=int, default=2,
+                    help="steps in flight in the timed serving loop (1-4)")
     ap.add_argument("--group", type=int, default=0, metavar="R",
                     help="also time R requests of the workload's shape, each with its own "
                          "prefix, in one grouped attention launch")
@@ -408,7 +410,7 @@ def main():
     step = blink.ScoringStep(tables.tail_len, tables.cand_ids, tables.cand_off, tensors,
                              cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
                              cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream,
-                             readout=args.readout, depth=2)
+                             readout=args.readout, depth=args.depth)
     label_pack_ms = None
     if step.readout_form == "batched":
         # The distinct-row table is built once per request, with the option table's upload;
@@ -448,7 +450,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         step.submit()
-        if step.outstanding() == 2:
+        if step.outstanding() == args.depth:
             step.collect()
     while step.outstanding():
         step.collect()

@@ -76,8 +76,8 @@ class ScoringStep:
     argmax straight into one pinned host buffer. Those host buffers are reused, so a step
     queued with ``run(fetch=False)`` must be synchronised before the next step is packed.
 
-    ``depth`` (1 or 2) is the number of steps that may be in flight. With 2, a second slot has
-    its own pinned row tables and results, its own device row tables, attention output and
+    ``depth`` (1 to 4) is the number of steps that may be in flight. Each slot beyond the first
+    has its own pinned row tables and results, its own device row tables, attention output and
     logits, and its own stream (default priority), so step k + 1 can be packed and queued with
     ``submit()`` while step k still runs, and its kernels can start on compute units that
     step k's last workgroups leave idle; ``collect()`` waits for the oldest step and returns its
@@ -97,8 +97,8 @@ class ScoringStep:
         import torch
 
         self.torch = torch
-        if depth not in (1, 2):
-            raise BlinkError(BLINK_E_INVALID, "depth must be 1 or 2")
+        if depth not in (1, 2, 3, 4):
+            raise BlinkError(BLINK_E_INVALID, "depth must be 1 to 4")
         self.tail_len = np.ascontiguousarray(np.asarray(tail_len, np.int32))
         n = self.n = int(self.tail_len.shape[0])
         self.prefix_len = int(prefix_len)

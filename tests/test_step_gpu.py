@@ -174,3 +174,25 @@ def test_pipelined_full_size_is_bitwise_sequential():
     for out in (step.out, step._slots[1].keep[1]):
         assert torch.equal(out[rows].view(torch.int16), out0[rows].view(torch.int16))
     print("  six overlapped steps bitwise equal to a synchronised one", flush=True)
+
+
+def test_three_steps_in_flight():
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(1)
+    req = Request(cfg)
+    ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
+    step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows, depth=3)
+    z, p, a = label_readout(req.tensors["hidden"], req.pack["last_row"], req.tensors["w_u"],
+                            req.tables.cand_ids, req.tables.cand_off, cfg.temperature)
+    for _ in range(3):
+        step.submit()
+    with pytest.raises(blink.BlinkError):
+        step.submit()
+    for _ in range(3):
+        probs, arg = step.collect()
+        assert float(np.abs(probs - p).max()) <= PROB_TOL
+        check_argmax(z, req.tables.cand_off, a, arg)
+    step.close()
