@@ -10,10 +10,10 @@
 // unembedding rows, M small (questions x score_len) and V = 151936, so W must be read from
 // HBM exactly once while H (M x d_model, a few MB) is re-read from L2:
 //  * score_partials_kernel: one workgroup per 128-row slice of the vocabulary and per block
-//    of up to 256 scored rows (128 for calls of at most 128 rows). Both operands go through LDS in chunks of 64 hidden elements
-//    (a 128 x 64 slice of W and a 256 x 64 slice of H, rows padded by 16 bytes), and each
-//    wave computes Z^T for its 32 rows with v_mfma_f32_32x32x16_bf16 (4 vocabulary
-//    tiles of 32). Computing Z^T puts one scored row per lane (and its partner lane l ^ 32),
+//    of up to 256 scored rows (128 for calls of at most 128 rows). Both operands go through
+//    LDS in chunks of 64 hidden elements (a 128 x 64 slice of W and a 256 x 64 slice of H,
+//    rows padded by 16 bytes), and each wave computes Z^T for its 32 rows with
+//    v_mfma_f32_32x32x16_bf16 (4 vocabulary tiles of 32). Computing Z^T puts one scored row per lane (and its partner lane l ^ 32),
 //    so the slice's maximum and sum of exp are lane-local but for one exchange. The slice
 //    writes (max, sum of exp(z - max)) per row to the workspace, and the logit of the row's
 //    target if the target falls in the slice.
