@@ -13,10 +13,10 @@
 //    of up to 256 scored rows (128 for calls of at most 128 rows). Both operands go through
 //    LDS in chunks of 64 hidden elements (a 128 x 64 slice of W and a 256 x 64 slice of H,
 //    rows padded by 16 bytes), and each wave computes Z^T for its 32 rows with
-//    v_mfma_f32_32x32x16_bf16 (4 vocabulary tiles of 32). Computing Z^T puts one scored row per lane (and its partner lane l ^ 32),
-//    so the slice's maximum and sum of exp are lane-local but for one exchange. The slice
-//    writes (max, sum of exp(z - max)) per row to the workspace, and the logit of the row's
-//    target if the target falls in the slice.
+//    v_mfma_f32_32x32x16_bf16 (4 vocabulary tiles of 32). Computing Z^T puts one scored row
+//    per lane (and its partner lane l ^ 32), so the slice's maximum and sum of exp are
+//    lane-local but for one exchange. The slice writes (max, sum of exp(z - max)) per row to
+//    the workspace, and the logit of the row's target if the target falls in the slice.
 //  * score_finish_kernel: one wave per scored row merges its slices' (max, sum) pairs into the
 //    log-sum-exp and subtracts it from the target's logit.
 #include <hip/hip_runtime.h>
