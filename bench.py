@@ -457,6 +457,16 @@ def main():
     torch.cuda.synchronize()
     elapsed_pipelined = time.perf_counter() - t0
 
+    # Untimed check: overlapped steps give bitwise the results of a synchronised step.
+    ref_probs, ref_arg = (x.copy() for x in step.run())
+    for i in range(2 * args.depth):
+        step.submit()
+        if step.outstanding() == args.depth or i == 2 * args.depth - 1:
+            while step.outstanding():
+                probs, arg = step.collect()
+                if not (np.array_equal(probs, ref_probs) and np.array_equal(arg, ref_arg)):
+                    raise RuntimeError("overlapped steps differ from a synchronised step")
+
     attn_each = np.array([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)])
     read_each = np.array([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)])
     ev.close()
@@ -534,6 +544,7 @@ def main():
             # One step at a time, each synchronised before the next is packed (the loop the
             # kernel times above come from).
             "sequential_questions_per_s": n * args.steps / elapsed,
+            "overlapped_steps_checked_bitwise": True,
             "sequential_ms_per_step": elapsed * 1e3 / args.steps,
             "readout_form": step.readout_form,
             "label_rows": (None if step.label_rows is None else int(step.label_rows.n_rows)),
