@@ -23,7 +23,10 @@ It follows the blink.py page (thegovind/blink-4b):
                      answer_for);
   * ``scoring``   -- teacher-forced scoring of a sequence's last tokens: full-vocabulary
                      log-softmax at each scored row, read at the next token (the simit MoT
-                     engine page: score_len).
+                     engine page: score_len);
+  * ``refine``    -- rotation averaging of label log-probabilities with an optional
+                     content-free prior, and the two-stage choice's finalists (the ruling
+                     page: _score_plain, TwoStageChoice).
 
 Arithmetic is float64 throughout; bf16 inputs are widened exactly.
 Every function is pinned by tests under ``tests/test_oracle_*.py``; none is "parity unpinned".
@@ -42,6 +45,7 @@ from .path import score_request
 from .prefix import plan_prefix, shared_prefix_len, PREFIX_MIN_TOKENS
 from .answers import answer_for, assemble
 from .scoring import score_rows, teacher_forced_logprobs
+from .refine import combine_rotations, scatter_finalists, two_stage_finalists
 
 __all__ = [
     "pack_ragged",
@@ -66,4 +70,7 @@ __all__ = [
     "assemble",
     "score_rows",
     "teacher_forced_logprobs",
+    "combine_rotations",
+    "scatter_finalists",
+    "two_stage_finalists",
 ]
