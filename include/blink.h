@@ -58,7 +58,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 6
+#define BLINK_ABI_VERSION 7
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -338,6 +338,42 @@ int blink_score_targets(const void *hidden, int64_t hidden_rows, int32_t d_model
                         const int64_t *d_rows, const int32_t *d_targets, int32_t n_rows,
                         const void *w_u, int64_t vocab, float *d_logprob, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * blink_combine_rotations -- host, synchronous.
+ *
+ * Rotation averaging of label log-probabilities (the ruling page, _score_plain): a question
+ * may be read in several passes, each presenting its options in another order. For every pass
+ * the label logits become log-probabilities over that pass's options (log-softmax, double
+ * precision); when `prior` is given, the content-free prior's log-probability of each position
+ * is subtracted; each option key's result is the mean over the passes that offered it.
+ *
+ *   pass_logits[sum], pass_off[n_passes+1]  each pass's logits by position (CSR)
+ *   pass_question[n_passes]   the question each pass reads (0..n_questions-1)
+ *   pass_key[sum]             the option key each position presents (0..K_q-1)
+ *   prior[sum]                NULL, or the prior log-probability of each position
+ *   key_off[n_questions+1]    CSR of the questions' option keys (1..255 each)
+ *   mean_logprob[key_off[n]]  output: mean log-probability per key; NaN if no pass offered it
+ * Malformed tables are BLINK_E_INVALID / BLINK_E_LIMIT, naming the pass or position.
+ */
+int blink_combine_rotations(const float *pass_logits, const int32_t *pass_off,
+                            const int32_t *pass_question, const int32_t *pass_key,
+                            const float *prior, int32_t n_passes, const int32_t *key_off,
+                            int32_t n_questions, float *mean_logprob);
+
+/*
+ * blink_two_stage_finalists -- host, synchronous.
+ *
+ * The two-stage choice for option lists wider than one pass (the ruling page,
+ * TwoStageChoice): options ranked by their stage-one score, highest first and earlier options
+ * first on ties, keep their first `keep` (at least 1) as finalists. The final choice then
+ * scores only the finalists; every other option gets a score of minus infinity.
+ *
+ *   stage_one[n_options]   1..255 scores, none NaN
+ *   finalists[min(keep, n_options)]   output option indices, best first; n_finalists output
+ */
+int blink_two_stage_finalists(const float *stage_one, int32_t n_options, int32_t keep,
+                              int32_t *finalists, int32_t *n_finalists);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,7 @@ from ._binding import (
     ANSWER_SCORE,
     assemble_answers,
     check_candidate_table,
+    combine_rotations,
     encode_prefix_attention,
     label_readout,
     label_readout_batched,
@@ -42,6 +43,7 @@ from ._binding import (
     pack_labels,
     pack_ragged,
     plan_prefix,
+    two_stage_finalists,
     prefix_tail_attention,
 )
 from .path import ScoringStep, label_name
@@ -71,6 +73,8 @@ __all__ = [
     "ANSWER_SCORE",
     "assemble_answers",
     "check_candidate_table",
+    "combine_rotations",
+    "two_stage_finalists",
     "encode_prefix_attention",
     "label_readout",
     "label_readout_batched",

@@ -41,6 +41,8 @@ EXPORTS = (
     "blink_prefix_tail_attention_grouped",
     "blink_score_targets_workspace",
     "blink_score_targets",
+    "blink_combine_rotations",
+    "blink_two_stage_finalists",
 )
 
 
@@ -111,6 +113,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.blink_score_targets.restype = ctypes.c_int
     lib.blink_score_targets.argtypes = [_P, _I64, _I32, _P, _P, _I32, _P, _I64, _P, _P,
                                         ctypes.c_size_t, _P]
+    _PF = ctypes.POINTER(ctypes.c_float)
+    lib.blink_combine_rotations.restype = ctypes.c_int
+    lib.blink_combine_rotations.argtypes = [_PF, _PI32, _PI32, _PI32, _PF, _I32, _PI32, _I32,
+                                            _PF]
+    lib.blink_two_stage_finalists.restype = ctypes.c_int
+    lib.blink_two_stage_finalists.argtypes = [_PF, _I32, _I32, _PI32, _PI32]
     lib.blink_plan_prefix.restype = ctypes.c_int
     lib.blink_plan_prefix.argtypes = [_PI32, _PI64, _I32, _I32, _PI32, _PI32, _PI64]
     _lib = lib
@@ -322,6 +330,47 @@ def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offs
     if not launch:
         return args
     _check(lib.blink_prefix_tail_attention(*args))
+
+
+def combine_rotations(n_keys, passes, priors=None) -> list:
+    """Rotation averaging (blink_combine_rotations). n_keys[q]: options of question q;
+    passes: (question, key of each position, logits of each position); priors: None or per
+    pass the prior log-probability of each position. Returns per question a float32 array of
+    mean log-probabilities per key (NaN where no pass offered the key)."""
+    lib = load_library()
+    f32 = ctypes.POINTER(ctypes.c_float)
+    key_off = np.concatenate([[0], np.cumsum(n_keys)]).astype(np.int32)
+    pass_off = np.concatenate([[0], np.cumsum([len(p[1]) for p in passes])]).astype(np.int32)
+    pq = np.asarray([p[0] for p in passes], np.int32)
+    keys = np.ascontiguousarray(np.concatenate([np.asarray(p[1], np.int32) for p in passes])
+                                if passes else np.zeros(1, np.int32))
+    logits = np.ascontiguousarray(np.concatenate([np.asarray(p[2], np.float32) for p in passes])
+                                  if passes else np.zeros(1, np.float32))
+    prior = None
+    if priors is not None:
+        prior = np.ascontiguousarray(np.concatenate([np.asarray(x, np.float32) for x in priors]))
+        if prior.shape[0] != logits.shape[0]:
+            raise BlinkError(BLINK_E_INVALID, "priors must give one value per pass position")
+    out = np.zeros(max(int(key_off[-1]), 1), np.float32)
+    pq_src = pq if pq.size else np.zeros(1, np.int32)
+    _check(lib.blink_combine_rotations(
+        logits.ctypes.data_as(f32), _ptr(pass_off, ctypes.c_int32), _ptr(pq_src, ctypes.c_int32),
+        _ptr(keys, ctypes.c_int32), None if prior is None else prior.ctypes.data_as(f32),
+        len(passes), _ptr(key_off, ctypes.c_int32), len(n_keys), out.ctypes.data_as(f32)))
+    return [out[key_off[q]:key_off[q + 1]] for q in range(len(n_keys))]
+
+
+def two_stage_finalists(stage_one, keep: int) -> np.ndarray:
+    """Finalists of a two-stage choice (blink_two_stage_finalists), best first."""
+    lib = load_library()
+    s1 = np.ascontiguousarray(np.asarray(stage_one, np.float32))
+    out = np.zeros(max(int(s1.shape[0]), 1), np.int32)
+    k = ctypes.c_int32(0)
+    src = s1 if s1.size else np.zeros(1, np.float32)
+    _check(lib.blink_two_stage_finalists(src.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                         int(s1.shape[0]), int(keep),
+                                         _ptr(out, ctypes.c_int32), ctypes.byref(k)))
+    return out[:k.value]
 
 
 class GroupedAttention:

@@ -289,3 +289,84 @@ extern "C" int blink_assemble_answers(const float *probs, const int32_t *cand_of
   }
   return blink::ok();
 }
+
+// Rotation averaging (ruling page, _score_plain): each pass's label logits become
+// log-probabilities over the pass's own options (log-softmax, in double); a prior's
+// log-probabilities for the same positions are subtracted when given; every option key's
+// result is the mean over the passes that offered it (NaN if none did).
+extern "C" int blink_combine_rotations(const float *pass_logits, const int32_t *pass_off,
+                                       const int32_t *pass_question, const int32_t *pass_key,
+                                       const float *prior, int32_t n_passes,
+                                       const int32_t *key_off, int32_t n_questions,
+                                       float *mean_logprob) {
+  using blink::fail;
+  if (!pass_logits || !pass_off || !pass_question || !pass_key || !key_off || !mean_logprob)
+    return fail(BLINK_E_INVALID, "blink_combine_rotations: a pointer argument is NULL");
+  if (n_passes < 1 || n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
+    return fail(BLINK_E_LIMIT, "%d passes over %d questions; need 1 or more passes and 1-%d "
+                "questions", n_passes, n_questions, BLINK_MAX_QUESTIONS);
+  if (pass_off[0] != 0 || key_off[0] != 0)
+    return fail(BLINK_E_INVALID, "offsets must start at 0");
+  for (int q = 0; q < n_questions; ++q)
+    if (key_off[q + 1] - key_off[q] < 1 || key_off[q + 1] - key_off[q] > BLINK_MAX_OPTIONS)
+      return fail(BLINK_E_LIMIT, "%d options per choice; supported 1-%d",
+                  key_off[q + 1] - key_off[q], BLINK_MAX_OPTIONS);
+  for (int p = 0; p < n_passes; ++p) {
+    const int q = pass_question[p];
+    const int k = pass_off[p + 1] - pass_off[p];
+    if (q < 0 || q >= n_questions)
+      return fail(BLINK_E_INVALID, "pass %d names question %d of %d", p, q, n_questions);
+    if (k < 1 || k > key_off[q + 1] - key_off[q])
+      return fail(BLINK_E_INVALID, "pass %d offers %d options; its question has %d", p, k,
+                  key_off[q + 1] - key_off[q]);
+    for (int i = pass_off[p]; i < pass_off[p + 1]; ++i)
+      if (pass_key[i] < 0 || pass_key[i] >= key_off[q + 1] - key_off[q])
+        return fail(BLINK_E_INVALID, "pass %d position %d names key %d", p, i - pass_off[p],
+                    pass_key[i]);
+  }
+  const int total = key_off[n_questions];
+  std::vector<double> sum(size_t(total), 0.0);
+  std::vector<int32_t> count(size_t(total), 0);
+  for (int p = 0; p < n_passes; ++p) {
+    const int lo = pass_off[p], hi = pass_off[p + 1];
+    double m = -INFINITY;
+    for (int i = lo; i < hi; ++i) m = std::max(m, double(pass_logits[i]));
+    double s = 0.0;
+    for (int i = lo; i < hi; ++i) s += std::exp(double(pass_logits[i]) - m);
+    const double lse = m + std::log(s);
+    const int base = key_off[pass_question[p]];
+    for (int i = lo; i < hi; ++i) {
+      double v = double(pass_logits[i]) - lse;
+      if (prior) v -= double(prior[i]);
+      sum[size_t(base + pass_key[i])] += v;
+      ++count[size_t(base + pass_key[i])];
+    }
+  }
+  for (int j = 0; j < total; ++j)
+    mean_logprob[j] = count[size_t(j)] ? float(sum[size_t(j)] / count[size_t(j)]) : NAN;
+  return blink::ok();
+}
+
+// Two-stage choice (ruling page, TwoStageChoice): the options ranked by their stage-one score,
+// highest first and earlier options first on ties, keep their first `keep` as finalists.
+extern "C" int blink_two_stage_finalists(const float *stage_one, int32_t n_options,
+                                         int32_t keep, int32_t *finalists,
+                                         int32_t *n_finalists) {
+  using blink::fail;
+  if (!stage_one || !finalists || !n_finalists)
+    return fail(BLINK_E_INVALID, "blink_two_stage_finalists: a pointer argument is NULL");
+  if (n_options < 1 || n_options > BLINK_MAX_OPTIONS)
+    return fail(BLINK_E_LIMIT, "%d options per choice; supported 1-%d", n_options,
+                BLINK_MAX_OPTIONS);
+  if (keep < 1) return fail(BLINK_E_INVALID, "keep must be at least 1");
+  for (int i = 0; i < n_options; ++i)
+    if (std::isnan(stage_one[i])) return fail(BLINK_E_INVALID, "stage-one score %d is NaN", i);
+  std::vector<int32_t> order(static_cast<size_t>(n_options));
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return stage_one[a] > stage_one[b]; });
+  const int k = std::min(keep, n_options);
+  for (int i = 0; i < k; ++i) finalists[i] = order[size_t(i)];
+  *n_finalists = k;
+  return blink::ok();
+}

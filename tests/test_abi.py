@@ -13,6 +13,7 @@ from oracle.pack import pack_ragged as oracle_pack
 from oracle.readout import label_rows as oracle_label_rows
 from oracle.prefix import plan_prefix as oracle_plan_prefix
 from oracle.answers import assemble as oracle_assemble
+from oracle import refine as oracle_refine
 
 HEADER = os.path.join(ROOT, "include", "blink.h")
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 6
+    assert blink.load_library().blink_abi_version() == 7
 
 
 def _compare(pk, ref):
@@ -432,3 +433,53 @@ def test_score_targets_refusals_before_launch(blink, kw, code, msg):
     lib = blink.load_library()
     assert _score(lib, **kw) == code
     assert msg in lib.blink_last_error().decode()
+
+
+def test_combine_rotations_matches_oracle_random(blink):
+    rng = np.random.default_rng(11)
+    for trial in range(100):
+        nq = int(rng.integers(1, 20))
+        n_keys = rng.integers(1, 30, size=nq).tolist()
+        passes, priors = [], []
+        for _ in range(int(rng.integers(1, 60))):
+            q = int(rng.integers(nq))
+            k = n_keys[q]
+            shown = rng.permutation(k)[:int(rng.integers(1, k + 1))].tolist()
+            logits = (rng.standard_normal(len(shown)) * 3).astype(np.float32)
+            passes.append((q, shown, logits))
+            priors.append(np.log(rng.dirichlet(np.ones(len(shown)))).astype(np.float32))
+        use_prior = trial % 2 == 0
+        got = blink.combine_rotations(n_keys, passes, priors if use_prior else None)
+        ref = oracle_refine.combine_rotations(
+            n_keys, [(q, keys, [float(v) for v in lg]) for q, keys, lg in passes],
+            [[float(v) for v in p] for p in priors] if use_prior else None)
+        for g, r in zip(got, ref):
+            r = np.asarray(r)
+            assert np.array_equal(np.isnan(g), np.isnan(r))
+            np.testing.assert_allclose(g[~np.isnan(g)], r[~np.isnan(r)], rtol=0, atol=2e-6)
+
+
+def test_two_stage_finalists_matches_oracle_random(blink):
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        n = int(rng.integers(1, 256))
+        s1 = np.round(rng.standard_normal(n) * 2, int(rng.integers(0, 3))).astype(np.float32)
+        keep = int(rng.integers(1, 300))
+        got = blink.two_stage_finalists(s1, keep)
+        assert got.tolist() == oracle_refine.two_stage_finalists([float(v) for v in s1], keep)
+
+
+@pytest.mark.parametrize("call, msg", [
+    (lambda b: b.combine_rotations([2], [(1, [0, 1], [0.0, 0.0])]), "pass 0 names question 1"),
+    (lambda b: b.combine_rotations([2], [(0, [0, 2], [0.0, 0.0])]), "names key 2"),
+    (lambda b: b.combine_rotations([2], [(0, [0, 1, 0], [0.0, 0.0, 0.0])]), "offers 3 options"),
+    (lambda b: b.combine_rotations([2], []), "0 passes"),
+    (lambda b: b.combine_rotations([256], [(0, [0], [0.0])]), "256 options per choice"),
+    (lambda b: b.two_stage_finalists([1.0, float("nan")], 1), "stage-one score 1 is NaN"),
+    (lambda b: b.two_stage_finalists([1.0], 0), "keep must be at least 1"),
+    (lambda b: b.two_stage_finalists([0.0] * 256, 3), "256 options per choice"),
+])
+def test_refinement_refusals(blink, call, msg):
+    with pytest.raises(blink.BlinkError) as e:
+        call(blink)
+    assert msg in str(e.value)
