@@ -102,3 +102,42 @@ def test_malformed_entries_are_flagged(number):
     sub_off = np.concatenate([[0], np.cumsum([off[i + 1] - off[i] for i in good])])
     sub = np.concatenate([np.arange(off[i], off[i + 1]) for i in good])
     check_argmax(z[sub], sub_off, a[good], arg[good])
+
+
+def test_rotations_through_the_readout():
+    # Each question is read in three rotations of its option order (each rotation a question
+    # of its own in one readout call); the GPU logits, combined per key on the host, must
+    # match the same combination of the FP64 oracle's logits.
+    import pass_typed_decision_amd as blink
+    from oracle.readout import label_readout as oracle_readout
+    from oracle.refine import combine_rotations as oracle_combine
+
+    cfg = synth.config(2)
+    req = Request(cfg, parts=READOUT_PARTS)
+    ids, off = req.tables.cand_ids, req.tables.cand_off
+    last = np.asarray(req.pack["last_row"], np.int64)
+    n = len(off) - 1
+    r_ids, r_last, r_counts, passes_meta = [], [], [], []
+    for i in range(n):
+        k = int(off[i + 1] - off[i])
+        for r in range(3):
+            order = [(r + j) % k for j in range(k)]
+            r_ids.extend(int(ids[off[i] + o]) for o in order)
+            r_last.append(int(last[i]))
+            r_counts.append(k)
+            passes_meta.append((i, order))
+    r_off = np.concatenate([[0], np.cumsum(r_counts)]).astype(np.int32)
+    r_ids = np.asarray(r_ids, np.int32)
+    logits, _, _ = run_readout(req, last_row=np.asarray(r_last, np.int64), cand_ids=r_ids,
+                               cand_off=r_off)
+    z, _, _ = oracle_readout(req.tensors["hidden"], r_last, req.tensors["w_u"], r_ids, r_off,
+                             cfg.temperature)
+    n_keys = np.diff(off).tolist()
+    gpu_passes = [(q, order, logits[r_off[p]:r_off[p + 1]])
+                  for p, (q, order) in enumerate(passes_meta)]
+    ref_passes = [(q, order, z[r_off[p]:r_off[p + 1]]) for p, (q, order) in enumerate(passes_meta)]
+    got = blink.combine_rotations(n_keys, gpu_passes)
+    ref = oracle_combine(n_keys, ref_passes)
+    err = max(float(np.abs(g - np.asarray(r)).max()) for g, r in zip(got, ref))
+    print(f"  rotations of {n} questions: max abs err {err:.2e}", flush=True)
+    assert err <= LOGIT_TOL
