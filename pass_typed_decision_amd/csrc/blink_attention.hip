@@ -127,11 +127,15 @@ struct Args {
   // launch gives each request its own units (no unit spans two requests, so each unit has
   // exactly one prefix): request r holds questions [req_first[r], req_first[r+1]), units
   // [req_unit[r], req_unit[r+1]) and prefix rows [req_pstart[r], req_pstart[r] + req_plen[r]).
+  // Its first req_full[r] units hold kRowsPerUnit rows each, the later ones req_small[r] rows
+  // each (see grouped_split).
   int n_req;
   int req_first[kMaxRequests + 1];
   int64_t req_unit[kMaxRequests + 1];
   int64_t req_pstart[kMaxRequests];
   int req_plen[kMaxRequests];
+  int req_full[kMaxRequests];
+  int req_small[kMaxRequests];
 };
 
 template <int D>
@@ -775,9 +779,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     int r = 0;  // the unit's request: the last r with req_unit[r] <= unit
     while (r + 1 < a.n_req && a.req_unit[r + 1] <= unit) ++r;
     const int64_t rows_end = int64_t(uniform(sm.tab.start[a.req_first[r + 1]])) * G;
+    const int64_t k = unit - a.req_unit[r], full = a.req_full[r], small = a.req_small[r];
     row0 = int64_t(uniform(sm.tab.start[a.req_first[r]])) * G +
-           (unit - a.req_unit[r]) * kRowsPerUnit;
-    row_end = min(rows_end, row0 + kRowsPerUnit);
+           (k < full ? k * kRowsPerUnit : full * kRowsPerUnit + (k - full) * small);
+    row_end = min(rows_end, row0 + (k < full ? int64_t(kRowsPerUnit) : small));
     u.plen = a.req_plen[r];
     u.pstart = a.req_pstart[r];
   }
@@ -912,6 +917,47 @@ inline int64_t unit_split(int64_t rows, int hkv, int cus, int64_t &full_units, i
   full_units = full;
   small_rows = int(small_up);
   return full + (rem + small_up - 1) / small_up;
+}
+
+// Work split of a grouped launch, with `rows[r]` query rows per KV head in request r: the
+// same idea as unit_split, with no unit spanning two requests. Each request is cut into units
+// of kRowsPerUnit rows. The units beyond the last full round of workgroups (the last ones in
+// unit order, so they may span several requests) are re-cut, request by request, into units
+// of the smallest multiple of 4 waves' rows that still fits them in one round; a launch of
+// less than one round is cut the same way from the start. Fills full[r] (units of
+// kRowsPerUnit rows) and small[r] (rows of each later unit) and returns the units per head.
+inline int64_t grouped_split(const int64_t *rows, int n_req, int hkv, int cus, int *full,
+                             int *small) {
+  int64_t units = 0;
+  for (int r = 0; r < n_req; ++r) {
+    full[r] = int((rows[r] + kRowsPerUnit - 1) / kRowsPerUnit);
+    small[r] = kRowsPerUnit;
+    units += full[r];
+  }
+  const int64_t per_round = cus / hkv;  // units of one head in one round
+  const int64_t simd_rows = 4 * kRowsPerWave;  // one wave on each SIMD
+  if (per_round < 1) return units;
+  const int64_t lead = units <= per_round ? 0 : units / per_round * per_round;  // kept whole
+  if (lead == units) return units;
+  int64_t keep[kMaxRequests];  // whole units a request keeps ahead of the re-cut ones
+  int64_t seen = 0;
+  for (int r = 0; r < n_req; ++r) {
+    keep[r] = min(int64_t(full[r]), max(int64_t(0), lead - seen));
+    seen += full[r];
+  }
+  for (int64_t s = simd_rows; s < kRowsPerUnit; s += simd_rows) {
+    int64_t cut = 0;
+    for (int r = 0; r < n_req; ++r)
+      if (keep[r] < full[r]) cut += (rows[r] - keep[r] * kRowsPerUnit + s - 1) / s;
+    if (cut > per_round) continue;
+    for (int r = 0; r < n_req; ++r)
+      if (keep[r] < full[r]) {
+        full[r] = int(keep[r]);
+        small[r] = int(s);
+      }
+    return lead + cut;
+  }
+  return units;
 }
 
 template <int D>
@@ -1073,7 +1119,7 @@ extern "C" int blink_prefix_tail_attention_grouped(
   a.n_req = n_requests;
   a.full_units = 0;
   a.small_rows = kRowsPerUnit;
-  int64_t units = 0;
+  int64_t rows[kMaxRequests];
   for (int r = 0; r < n_requests; ++r) {
     const int f = h_request_first[r], l = h_request_first[r + 1];
     if (l <= f) return fail(BLINK_E_INVALID, "request %d has no questions", r);
@@ -1090,11 +1136,18 @@ extern "C" int blink_prefix_tail_attention_grouped(
                     "context length of %d", i, (long long)total, BLINK_MAX_INPUT_TOKENS);
     }
     a.req_first[r] = f;
-    a.req_unit[r] = units;
     a.req_pstart[r] = ps;
     a.req_plen[r] = pl;
-    const int64_t rows = int64_t(h_valid_start[l] - h_valid_start[f]) * G;
-    units += (rows + kRowsPerUnit - 1) / kRowsPerUnit;
+    rows[r] = int64_t(h_valid_start[l] - h_valid_start[f]) * G;
+  }
+  int cus = 0;
+  if ((rc = device_cus(cus)) != BLINK_OK) return rc;
+  grouped_split(rows, n_requests, n_heads_kv, cus, a.req_full, a.req_small);
+  int64_t units = 0;  // the grid and the kernel's unit -> rows map follow the same counts
+  for (int r = 0; r < n_requests; ++r) {
+    a.req_unit[r] = units;
+    units += a.req_full[r] + (rows[r] - int64_t(a.req_full[r]) * kRowsPerUnit +
+                              a.req_small[r] - 1) / a.req_small[r];
   }
   a.req_first[n_requests] = n_questions;
   a.req_unit[n_requests] = units;
