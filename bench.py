@@ -37,7 +37,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # plus WRITE_SIZE (x1), keyed by workload number, with the sha256 of the kernel source they were
 # counted on; a changed kernel reports null until it is counted again.
 MEASURED_TRAFFIC = {
-    2: ("c4bbd623c741cf3a409163b2b7d3199900586d058de0f2f7528facacebb4d7db", 124026902),
+    2: ("bbcb34d7994238bd06183ac9a50e873e7e2f8d7ad3c389627400b3fb691e9ce1", 123589018),
 }
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 
