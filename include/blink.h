@@ -111,7 +111,7 @@ int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, int32_t pref
  *   cand_ids[total]   token id of each offered label, each in [0, vocab) (else
  *                     BLINK_E_INVALID, naming the entry)
  *   cand_off[n+1]     CSR offsets: cand_off[0] = 0, 1 <= K_i <= 255 (else BLINK_E_LIMIT,
- *                     "K options per choice; supported 1-255")
+ *                     "question with K options; the limit is 1 to 255")
  *   n_questions       1..512 (else BLINK_E_LIMIT)
  *   vocab             1..2^31
  * Outputs (host arrays the caller allocates for the worst case, U = total):
@@ -238,7 +238,7 @@ int blink_prefix_tail_attention_grouped(
  *   n_questions 1..512, total_candidates = cand_off[n] (host copy, sizes checks)
  *   max_options 1..255: upper bound of every K_i
  *   d_model     multiple of 8, 8..8192
- *   temperature finite and > 0 (else BLINK_E_INVALID, "temperature must be positive")
+ *   temperature finite and > 0 (else BLINK_E_INVALID, "temperature is not a positive finite number")
  *   d_logits    float32 [total_candidates] device output
  *   d_probs     float32 [total_candidates] output
  *   d_argmax    int32 [n] output; -1 (with NaN logits/probs) marks a question whose

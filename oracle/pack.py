@@ -66,11 +66,11 @@ def pack_ragged(tail_len, token_budget=TOKEN_BUDGET, max_rows=0, prefix_len=0,
     lengths = [int(x) for x in tail_len]
     n = len(lengths)
     if not 1 <= n <= MAX_QUESTIONS:
-        raise PackError(f"{n} questions; supported 1-{MAX_QUESTIONS}")
+        raise PackError(f"request of {n} questions; the limit is 1 to {MAX_QUESTIONS}")
     if prefix_len < 0:
         raise PackError("prefix length must be non-negative")
     if token_budget < 1:
-        raise PackError("token budget must be positive")
+        raise PackError("token budget is below 1")
     if max_rows < 0:
         raise PackError("row cap must be non-negative")
     for i, length in enumerate(lengths):
@@ -78,8 +78,8 @@ def pack_ragged(tail_len, token_budget=TOKEN_BUDGET, max_rows=0, prefix_len=0,
             raise PackError(f"question {i} has an empty tail")
         if prefix_len + length > max_input_tokens:
             raise PackError(
-                f"question {i} renders to {prefix_len + length} tokens, over the maximum "
-                f"context length of {max_input_tokens}")
+                f"question {i} needs {prefix_len + length} tokens of context; the maximum "
+                f"context length is {max_input_tokens}")
 
     groups = _group(lengths, token_budget, max_rows)
     order, batch_first, batch_width, batch_base = [], [0], [], [0]

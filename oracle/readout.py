@@ -32,7 +32,7 @@ class ReadoutError(ValueError):
 def softmax_t(z, temperature):
     """Temperature softmax of one question's label scores, float64."""
     if not temperature > 0 or not math.isfinite(temperature):
-        raise ReadoutError("temperature must be positive")
+        raise ReadoutError("temperature is not a positive finite number")
     zt = np.asarray(z, dtype=np.float64) / float(temperature)
     e = np.exp(zt - zt.max())
     return e / e.sum()
@@ -61,7 +61,7 @@ def label_readout(hidden, last_row, w_u, cand_ids, cand_off, temperature):
     for i in range(n):
         lo, hi = cand_off[i], cand_off[i + 1]
         if not 1 <= hi - lo <= MAX_OPTIONS:
-            raise ReadoutError(f"{hi - lo} options per choice; supported 1-{MAX_OPTIONS}")
+            raise ReadoutError(f"question with {hi - lo} options; the limit is 1 to {MAX_OPTIONS}")
         ids = [int(c) for c in cand_ids[lo:hi]]
         if len(set(ids)) != len(ids):
             raise ReadoutError("label token ids collide")
@@ -120,7 +120,7 @@ def label_readout_batched(hidden, last_row, w_u, cand_ids, cand_off, temperature
     for i in range(n):
         lo, hi = cand_off[i], cand_off[i + 1]
         if not 1 <= hi - lo <= MAX_OPTIONS:
-            raise ReadoutError(f"{hi - lo} options per choice; supported 1-{MAX_OPTIONS}")
+            raise ReadoutError(f"question with {hi - lo} options; the limit is 1 to {MAX_OPTIONS}")
         ids = [int(c) for c in cand_ids[lo:hi]]
         if len(set(ids)) != len(ids):
             raise ReadoutError("label token ids collide")

@@ -598,7 +598,7 @@ def check_candidate_table(cand_ids, cand_off, vocab: int) -> int:
     k = np.diff(off)
     for i, ki in enumerate(k):
         if not 1 <= ki <= MAX_OPTIONS:
-            raise BlinkError(BLINK_E_LIMIT, f"{int(ki)} options per choice; supported 1-{MAX_OPTIONS}")
+            raise BlinkError(BLINK_E_LIMIT, f"question with {int(ki)} options; the limit is 1 to {MAX_OPTIONS}")
         row = ids[off[i]:off[i + 1]]
         if row.min() < 0 or row.max() >= vocab:
             raise BlinkError(BLINK_E_INVALID, f"question {i}: label token id out of range")

@@ -984,7 +984,7 @@ int check_shape(const void *q, const void *k_tail, const void *v_tail, const voi
                 const int64_t *d_token_offset, const int32_t *d_valid_start, const Shape &sh) {
   using blink::fail;
   if (sh.n_questions < 1 || sh.n_questions > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", sh.n_questions,
+    return fail(BLINK_E_LIMIT, "request of %d questions; the limit is 1 to %d", sh.n_questions,
                 BLINK_MAX_QUESTIONS);
   if (!q || !k_tail || !v_tail || !out || !d_token_offset || !d_valid_start)
     return fail(BLINK_E_INVALID, "prefix tail attention: a pointer argument is NULL");
@@ -1066,8 +1066,8 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
   int rc = check_shape(q, k_tail, v_tail, out, d_token_offset, d_valid_start, sh);
   if (rc != BLINK_OK) return rc;
   if (prefix_len < 0 || prefix_len >= BLINK_MAX_INPUT_TOKENS)
-    return fail(BLINK_E_LIMIT, "prefix of %d tokens leaves no room under the maximum context "
-                "length of %d", prefix_len, BLINK_MAX_INPUT_TOKENS);
+    return fail(BLINK_E_LIMIT, "prefix of %d tokens leaves no room for a tail; the maximum "
+                "context length is %d", prefix_len, BLINK_MAX_INPUT_TOKENS);
   if (prefix_len > 0 && (!k_prefix || !v_prefix))
     return fail(BLINK_E_INVALID, "prefix K/V pointers are NULL with prefix_len %d", prefix_len);
   int cus = 0;
@@ -1100,7 +1100,7 @@ extern "C" int blink_prefix_tail_attention_grouped(
   int rc = check_shape(q, k_tail, v_tail, out, d_token_offset, d_valid_start, sh);
   if (rc != BLINK_OK) return rc;
   if (n_requests < 1 || n_requests > kMaxRequests)
-    return fail(BLINK_E_LIMIT, "%d requests; supported 1-%d", n_requests, kMaxRequests);
+    return fail(BLINK_E_LIMIT, "group of %d requests; the limit is 1 to %d", n_requests, kMaxRequests);
   if (!h_valid_start || !h_request_first || !h_prefix_start || !h_prefix_len)
     return fail(BLINK_E_INVALID, "prefix tail attention: a pointer argument is NULL");
   if (total_prefix_rows < 0 || (total_prefix_rows > 0 && (!k_prefix || !v_prefix)))
@@ -1132,8 +1132,8 @@ extern "C" int blink_prefix_tail_attention_grouped(
     for (int i = f; i < l; ++i) {
       const int64_t total = int64_t(pl) + (h_valid_start[i + 1] - h_valid_start[i]);
       if (total > BLINK_MAX_INPUT_TOKENS)
-        return fail(BLINK_E_LIMIT, "question %d renders to %lld tokens, over the maximum "
-                    "context length of %d", i, (long long)total, BLINK_MAX_INPUT_TOKENS);
+        return fail(BLINK_E_LIMIT, "question %d needs %lld tokens of context; the maximum "
+                    "context length is %d", i, (long long)total, BLINK_MAX_INPUT_TOKENS);
     }
     a.req_first[r] = f;
     a.req_pstart[r] = ps;

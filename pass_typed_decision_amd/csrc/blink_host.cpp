@@ -55,9 +55,9 @@ extern "C" int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, i
       !total_padded_tokens || !total_valid_tokens)
     return fail(BLINK_E_INVALID, "blink_pack_ragged: a pointer argument is NULL");
   if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
+    return fail(BLINK_E_LIMIT, "request of %d questions; the limit is 1 to %d", n_questions, BLINK_MAX_QUESTIONS);
   if (prefix_len < 0) return fail(BLINK_E_INVALID, "prefix length must be non-negative");
-  if (token_budget < 1) return fail(BLINK_E_INVALID, "token budget must be positive");
+  if (token_budget < 1) return fail(BLINK_E_INVALID, "token budget is below 1");
   if (max_rows < 0) return fail(BLINK_E_INVALID, "row cap must be non-negative");
   const int n = n_questions;
   for (int i = 0; i < n; ++i) {
@@ -65,7 +65,7 @@ extern "C" int blink_pack_ragged(const int32_t *tail_len, int32_t n_questions, i
     const int64_t total = int64_t(prefix_len) + tail_len[i];
     if (total > BLINK_MAX_INPUT_TOKENS)
       return fail(BLINK_E_LIMIT,
-                  "question %d renders to %lld tokens, over the maximum context length of %d", i,
+                  "question %d needs %lld tokens of context; the maximum context length is %d", i,
                   (long long)total, BLINK_MAX_INPUT_TOKENS);
   }
 
@@ -137,14 +137,14 @@ extern "C" int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_of
   if (!cand_ids || !cand_off || !row_id || !row_first || !row_entry || !n_rows)
     return fail(BLINK_E_INVALID, "blink_pack_labels: a pointer argument is NULL");
   if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
+    return fail(BLINK_E_LIMIT, "request of %d questions; the limit is 1 to %d", n_questions, BLINK_MAX_QUESTIONS);
   if (vocab < 1 || vocab > (int64_t(1) << 31))
     return fail(BLINK_E_INVALID, "vocab %lld outside 1..2^31", (long long)vocab);
   if (cand_off[0] != 0) return fail(BLINK_E_INVALID, "candidate offsets must start at 0");
   for (int i = 0; i < n_questions; ++i) {
     const int64_t k = int64_t(cand_off[i + 1]) - cand_off[i];
     if (k < 1 || k > BLINK_MAX_OPTIONS)
-      return fail(BLINK_E_LIMIT, "%lld options per choice; supported 1-%d", (long long)k,
+      return fail(BLINK_E_LIMIT, "question with %lld options; the limit is 1 to %d", (long long)k,
                   BLINK_MAX_OPTIONS);
   }
   const int32_t total = cand_off[n_questions];
@@ -200,7 +200,7 @@ extern "C" int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, 
   if (!tokens || !seq_off || !shared_len || !prefix_len || !prefill_tokens)
     return fail(BLINK_E_INVALID, "blink_plan_prefix: a pointer argument is NULL");
   if (n_seqs < 1 || n_seqs > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_seqs, BLINK_MAX_QUESTIONS);
+    return fail(BLINK_E_LIMIT, "request of %d questions; the limit is 1 to %d", n_seqs, BLINK_MAX_QUESTIONS);
   if (min_prefix_tokens < 1)
     return fail(BLINK_E_INVALID, "the minimum shared prefix must be at least 1");
   if (seq_off[0] != 0) return fail(BLINK_E_INVALID, "sequence offsets must start at 0");
@@ -210,7 +210,7 @@ extern "C" int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, 
     if (len < 1) return fail(BLINK_E_INVALID, "sequence %d needs at least one token", i);
     if (len > BLINK_MAX_INPUT_TOKENS)
       return fail(BLINK_E_LIMIT,
-                  "question %d renders to %lld tokens, over the maximum context length of %d", i,
+                  "question %d needs %lld tokens of context; the maximum context length is %d", i,
                   (long long)len, BLINK_MAX_INPUT_TOKENS);
     shortest = std::min(shortest, len);
     total += len;
@@ -245,12 +245,12 @@ extern "C" int blink_assemble_answers(const float *probs, const int32_t *cand_of
   if (!probs || !cand_off || !qtype || !choice || !confidence || !value)
     return fail(BLINK_E_INVALID, "blink_assemble_answers: a pointer argument is NULL");
   if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
+    return fail(BLINK_E_LIMIT, "request of %d questions; the limit is 1 to %d", n_questions, BLINK_MAX_QUESTIONS);
   if (cand_off[0] != 0) return fail(BLINK_E_INVALID, "candidate offsets must start at 0");
   for (int i = 0; i < n_questions; ++i) {
     const int64_t k = int64_t(cand_off[i + 1]) - cand_off[i];
     if (k < 1 || k > BLINK_MAX_OPTIONS)
-      return fail(BLINK_E_LIMIT, "%lld options per choice; supported 1-%d", (long long)k,
+      return fail(BLINK_E_LIMIT, "question with %lld options; the limit is 1 to %d", (long long)k,
                   BLINK_MAX_OPTIONS);
     if (qtype[i] == BLINK_ANSWER_NOUL && k != 2)
       return fail(BLINK_E_INVALID, "question %d: a noul question offers exactly yes and no", i);
@@ -309,7 +309,7 @@ extern "C" int blink_combine_rotations(const float *pass_logits, const int32_t *
     return fail(BLINK_E_INVALID, "offsets must start at 0");
   for (int q = 0; q < n_questions; ++q)
     if (key_off[q + 1] - key_off[q] < 1 || key_off[q + 1] - key_off[q] > BLINK_MAX_OPTIONS)
-      return fail(BLINK_E_LIMIT, "%d options per choice; supported 1-%d",
+      return fail(BLINK_E_LIMIT, "question with %d options; the limit is 1 to %d",
                   key_off[q + 1] - key_off[q], BLINK_MAX_OPTIONS);
   for (int p = 0; p < n_passes; ++p) {
     const int q = pass_question[p];
@@ -356,7 +356,7 @@ extern "C" int blink_two_stage_finalists(const float *stage_one, int32_t n_optio
   if (!stage_one || !finalists || !n_finalists)
     return fail(BLINK_E_INVALID, "blink_two_stage_finalists: a pointer argument is NULL");
   if (n_options < 1 || n_options > BLINK_MAX_OPTIONS)
-    return fail(BLINK_E_LIMIT, "%d options per choice; supported 1-%d", n_options,
+    return fail(BLINK_E_LIMIT, "question with %d options; the limit is 1 to %d", n_options,
                 BLINK_MAX_OPTIONS);
   if (keep < 1) return fail(BLINK_E_INVALID, "keep must be at least 1");
   for (int i = 0; i < n_options; ++i)

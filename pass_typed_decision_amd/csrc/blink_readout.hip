@@ -415,11 +415,11 @@ int check_common(const void *hidden, int64_t hidden_rows, int32_t d_model,
                  const float *d_probs, const int32_t *d_argmax) {
   using blink::fail;
   if (!(temperature > 0.f) || !isfinite(temperature))
-    return fail(BLINK_E_INVALID, "temperature must be positive");
+    return fail(BLINK_E_INVALID, "temperature is not a positive finite number");
   if (n_questions < 1 || n_questions > BLINK_MAX_QUESTIONS)
-    return fail(BLINK_E_LIMIT, "%d questions; supported 1-%d", n_questions, BLINK_MAX_QUESTIONS);
+    return fail(BLINK_E_LIMIT, "request of %d questions; the limit is 1 to %d", n_questions, BLINK_MAX_QUESTIONS);
   if (max_options < 1 || max_options > BLINK_MAX_OPTIONS)
-    return fail(BLINK_E_LIMIT, "%d options per choice; supported 1-%d", max_options,
+    return fail(BLINK_E_LIMIT, "question with %d options; the limit is 1 to %d", max_options,
                 BLINK_MAX_OPTIONS);
   if (!hidden || !d_last_row || !w_u || !d_cand_off || !d_logits || !d_probs || !d_argmax)
     return fail(BLINK_E_INVALID, "label readout: a pointer argument is NULL");

@@ -227,7 +227,7 @@ extern "C" int blink_score_targets(const void *hidden, int64_t hidden_rows, int3
   if (!hidden || !d_rows || !d_targets || !w_u || !d_logprob || !workspace)
     return fail(BLINK_E_INVALID, "blink_score_targets: a pointer argument is NULL");
   if (n_rows < 1 || n_rows > kMaxRows)
-    return fail(BLINK_E_LIMIT, "%d scored rows; supported 1-%lld", n_rows, (long long)kMaxRows);
+    return fail(BLINK_E_LIMIT, "%d scored rows; the limit is 1 to %lld", n_rows, (long long)kMaxRows);
   if (d_model < kChunk || d_model > kMaxDModel || d_model % kChunk)
     return fail(BLINK_E_INVALID, "d_model %d must be a multiple of %d in %d..%d", d_model,
                 kChunk, kChunk, kMaxDModel);

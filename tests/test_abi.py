@@ -112,10 +112,10 @@ def test_prepared_pack_call_matches_pack_ragged(blink):
 
 
 @pytest.mark.parametrize("lengths, prefix, code, msg", [
-    ([], 0, -2, "0 questions; supported 1-512"),
-    ([1] * 513, 0, -2, "513 questions; supported 1-512"),
+    ([], 0, -2, "request of 0 questions; the limit is 1 to 512"),
+    ([1] * 513, 0, -2, "request of 513 questions; the limit is 1 to 512"),
     ([4, 0], 0, -1, "question 1 has an empty tail"),
-    ([5, 2], 131068, -2, "question 0 renders to 131073 tokens, over the maximum context length of 131072"),
+    ([5, 2], 131068, -2, "question 0 needs 131073 tokens of context; the maximum context length is 131072"),
     ([3], -1, -1, "prefix length must be non-negative"),
 ])
 def test_pack_refusals(blink, lengths, prefix, code, msg):
@@ -137,14 +137,14 @@ def _readout(lib, temperature=1.0, n=2, max_options=4, d_model=256, total=4):
 
 
 @pytest.mark.parametrize("kw, code, msg", [
-    (dict(temperature=0.0), -1, "temperature must be positive"),
-    (dict(temperature=-0.5), -1, "temperature must be positive"),
-    (dict(temperature=float("nan")), -1, "temperature must be positive"),
-    (dict(temperature=float("inf")), -1, "temperature must be positive"),
-    (dict(n=0), -2, "0 questions; supported 1-512"),
-    (dict(n=513), -2, "513 questions; supported 1-512"),
-    (dict(max_options=256), -2, "256 options per choice; supported 1-255"),
-    (dict(max_options=0), -2, "0 options per choice; supported 1-255"),
+    (dict(temperature=0.0), -1, "temperature is not a positive finite number"),
+    (dict(temperature=-0.5), -1, "temperature is not a positive finite number"),
+    (dict(temperature=float("nan")), -1, "temperature is not a positive finite number"),
+    (dict(temperature=float("inf")), -1, "temperature is not a positive finite number"),
+    (dict(n=0), -2, "request of 0 questions; the limit is 1 to 512"),
+    (dict(n=513), -2, "request of 513 questions; the limit is 1 to 512"),
+    (dict(max_options=256), -2, "question with 256 options; the limit is 1 to 255"),
+    (dict(max_options=0), -2, "question with 0 options; the limit is 1 to 255"),
     (dict(d_model=100), -1, "d_model 100 must be a multiple of 8"),
     (dict(total=1), -1, "does not fit"),
 ])
@@ -164,13 +164,13 @@ def _attention(lib, n=2, total=10, t_pad=12, prefix=0, hq=4, hkv=1, d=64, scale=
 
 
 @pytest.mark.parametrize("kw, code, msg", [
-    (dict(n=0), -2, "0 questions; supported 1-512"),
+    (dict(n=0), -2, "request of 0 questions; the limit is 1 to 512"),
     (dict(d=96), -1, "head_dim 96 is not supported"),
     (dict(hq=6, hkv=4), -1, "head counts 6/4"),
     (dict(hq=34, hkv=2), -1, "group <= 16"),
     (dict(scale=0.0), -1, "scale must be finite and positive"),
     (dict(prefix=5), -1, "prefix K/V pointers are NULL"),
-    (dict(prefix=131072, null_prefix=False), -2, "maximum context length of 131072"),
+    (dict(prefix=131072, null_prefix=False), -2, "maximum context length is 131072"),
     (dict(total=20, t_pad=12), -1, "token totals do not fit"),
     (dict(total=1), -1, "token totals do not fit"),
 ])
@@ -231,12 +231,12 @@ def test_pack_labels_matches_oracle_random(blink):
 
 
 @pytest.mark.parametrize("ids, off, vocab, code, msg", [
-    ([1, 2], [0, 2, 2], 10, -2, "0 options per choice; supported 1-255"),
-    (list(range(256)), [0, 256], 300, -2, "256 options per choice; supported 1-255"),
+    ([1, 2], [0, 2, 2], 10, -2, "question with 0 options; the limit is 1 to 255"),
+    (list(range(256)), [0, 256], 300, -2, "question with 256 options; the limit is 1 to 255"),
     ([1, 12], [0, 2], 10, -1, "option entry 1 has token id 12 outside [0, 10)"),
     ([-1], [0, 1], 10, -1, "option entry 0 has token id -1"),
     ([1], [0, 1], 0, -1, "vocab 0 outside"),
-    ([1], [0], 10, -2, "0 questions; supported 1-512"),
+    ([1], [0], 10, -2, "request of 0 questions; the limit is 1 to 512"),
 ])
 def test_pack_labels_refusals(blink, ids, off, vocab, code, msg):
     with pytest.raises(blink.BlinkError) as e:
@@ -254,9 +254,9 @@ def _readout_batched(lib, temperature=1.0, n=2, max_options=4, d_model=256, tota
 
 
 @pytest.mark.parametrize("kw, code, msg", [
-    (dict(temperature=0.0), -1, "temperature must be positive"),
-    (dict(n=513), -2, "513 questions; supported 1-512"),
-    (dict(max_options=256), -2, "256 options per choice; supported 1-255"),
+    (dict(temperature=0.0), -1, "temperature is not a positive finite number"),
+    (dict(n=513), -2, "request of 513 questions; the limit is 1 to 512"),
+    (dict(max_options=256), -2, "question with 256 options; the limit is 1 to 255"),
     (dict(d_model=12), -1, "d_model 12 must be a multiple of 8"),
     (dict(total=9), -1, "does not fit"),
     (dict(n_rows=0), -1, "n_rows 0 outside"),
@@ -303,11 +303,11 @@ def test_plan_prefix_at_the_context_limit(blink):
 
 
 @pytest.mark.parametrize("seqs, m, code, msg", [
-    ([], 256, -2, "0 questions; supported 1-512"),
-    ([[1]] * 513, 256, -2, "513 questions; supported 1-512"),
+    ([], 256, -2, "request of 0 questions; the limit is 1 to 512"),
+    ([[1]] * 513, 256, -2, "request of 513 questions; the limit is 1 to 512"),
     ([[1, 2], []], 256, -1, "sequence 1 needs at least one token"),
     ([[1, 2]], 0, -1, "the minimum shared prefix must be at least 1"),
-    ([[0] * 131073], 256, -2, "question 0 renders to 131073 tokens, over the maximum context length"),
+    ([[0] * 131073], 256, -2, "question 0 needs 131073 tokens of context; the maximum context length"),
 ])
 def test_plan_prefix_refusals(blink, seqs, m, code, msg):
     with pytest.raises(blink.BlinkError) as e:
@@ -351,12 +351,12 @@ def test_assemble_answers_matches_oracle_random(blink):
 
 
 @pytest.mark.parametrize("probs, off, types, code, msg", [
-    ([], [0], [], -2, "0 questions; supported 1-512"),
+    ([], [0], [], -2, "request of 0 questions; the limit is 1 to 512"),
     ([0.2, 0.3, 0.5], [0, 3], [1], -1, "a noul question offers exactly yes and no"),
     ([1.0], [0, 1], [2], -1, "a score takes 2 to 10 levels"),
     ([0.1] * 11, [0, 11], [2], -1, "a score takes 2 to 10 levels"),
     ([0.5, 0.5], [0, 2], [5], -1, "unknown question type 5"),
-    ([0.5, 0.5], [0, 2, 2], [0, 0], -2, "0 options per choice"),
+    ([0.5, 0.5], [0, 2, 2], [0, 0], -2, "question with 0 options"),
 ])
 def test_assemble_answers_refusals(blink, probs, off, types, code, msg):
     with pytest.raises(blink.BlinkError) as e:
@@ -384,9 +384,9 @@ def _ptr32(a):
 
 
 @pytest.mark.parametrize("kw, code, msg", [
-    (dict(first=(0,), pstart=(), plen=()), -2, "0 requests; supported 1-64"),
+    (dict(first=(0,), pstart=(), plen=()), -2, "group of 0 requests; the limit is 1 to 64"),
     (dict(first=tuple(range(66)), pstart=(0,) * 65, plen=(0,) * 65, n=65, total=65, t_pad=65,
-          vs=tuple(range(66))), -2, "65 requests; supported 1-64"),
+          vs=tuple(range(66))), -2, "group of 65 requests; the limit is 1 to 64"),
     (dict(first=(0, 2, 2)), -1, "request_first must run from 0 to n_questions"),
     (dict(first=(0, 3, 3)), -1, "request 1 has no questions"),
     (dict(first=(0, 0, 3)), -1, "request 0 has no questions"),
@@ -396,7 +396,7 @@ def _ptr32(a):
     (dict(vs=(0, 3, 5, 8)), -1, "valid_start must run from 0 to total_valid_tokens"),
     (dict(rows=0), -1, "prefix rows"),
     (dict(plen=(4, 131070), rows=131080, pstart=(0, 4)), -2,
-     "question 2 renders to 131074 tokens, over the maximum context length of 131072"),
+     "question 2 needs 131074 tokens of context; the maximum context length is 131072"),
 ])
 def test_grouped_attention_refusals_before_launch(blink, kw, code, msg):
     lib = blink.load_library()
@@ -474,10 +474,10 @@ def test_two_stage_finalists_matches_oracle_random(blink):
     (lambda b: b.combine_rotations([2], [(0, [0, 2], [0.0, 0.0])]), "names key 2"),
     (lambda b: b.combine_rotations([2], [(0, [0, 1, 0], [0.0, 0.0, 0.0])]), "offers 3 options"),
     (lambda b: b.combine_rotations([2], []), "0 passes"),
-    (lambda b: b.combine_rotations([256], [(0, [0], [0.0])]), "256 options per choice"),
+    (lambda b: b.combine_rotations([256], [(0, [0], [0.0])]), "question with 256 options"),
     (lambda b: b.two_stage_finalists([1.0, float("nan")], 1), "stage-one score 1 is NaN"),
     (lambda b: b.two_stage_finalists([1.0], 0), "keep must be at least 1"),
-    (lambda b: b.two_stage_finalists([0.0] * 256, 3), "256 options per choice"),
+    (lambda b: b.two_stage_finalists([0.0] * 256, 3), "question with 256 options"),
 ])
 def test_refinement_refusals(blink, call, msg):
     with pytest.raises(blink.BlinkError) as e:

@@ -84,8 +84,8 @@ def test_padded_rows_never_overlap():
 
 
 @pytest.mark.parametrize("bad, msg", [
-    ([], "questions; supported 1-512"),
-    ([1] * 513, "513 questions; supported 1-512"),
+    ([], "questions; the limit is 1 to 512"),
+    ([1] * 513, "request of 513 questions; the limit is 1 to 512"),
     ([3, 0], "empty tail"),
 ])
 def test_refused(bad, msg):
@@ -94,6 +94,6 @@ def test_refused(bad, msg):
 
 
 def test_context_limit():
-    with pytest.raises(PackError, match="over the maximum context length of 131072"):
+    with pytest.raises(PackError, match="the maximum context length is 131072"):
         pack_ragged([5, 2], prefix_len=131068)
     pack_ragged([4, 2], prefix_len=131068)  # exactly at the limit is accepted

@@ -101,16 +101,16 @@ def test_single_option_is_certain():
 
 @pytest.mark.parametrize("temperature", [0.0, -1.0, float("nan"), float("inf")])
 def test_bad_temperature(temperature):
-    with pytest.raises(ReadoutError, match="temperature must be positive"):
+    with pytest.raises(ReadoutError, match="temperature is not a positive finite number"):
         softmax_t([1.0, 2.0], temperature)
 
 
 def test_refusals():
     hidden = np.zeros((2, 2))
     w_u = np.zeros((300, 2))
-    with pytest.raises(ReadoutError, match="0 options per choice"):
+    with pytest.raises(ReadoutError, match="question with 0 options"):
         label_readout(hidden, [0], w_u, [], [0, 0], 1.0)
-    with pytest.raises(ReadoutError, match="256 options per choice; supported 1-255"):
+    with pytest.raises(ReadoutError, match="question with 256 options; the limit is 1 to 255"):
         label_readout(hidden, [0], w_u, list(range(256)), [0, 256], 1.0)
     with pytest.raises(ReadoutError, match="collide"):
         label_readout(hidden, [0], w_u, [4, 4], [0, 2], 1.0)
