@@ -18,6 +18,13 @@ ATTN_TOL = 2e-2  # max-abs on bf16 attention outputs
 PROB_TOL = 1e-4  # max-abs on label probabilities
 LOGIT_TOL = 1e-4
 ARGMAX_GAP = 1e-5  # argmax must match exactly where the oracle's top-2 logit gap exceeds this
+# max-abs on teacher-forced log-probabilities. Logits are FP32 sums of at most 5120 bf16
+# products (|z| ~ 1, rounding ~1e-6) and the log-sum-exp over 151936 FP32 terms adds a
+# relative ~1e-6, so the kernel's error is a few 1e-6 (2e-6 measured). 1e-4 leaves a wide
+# margin, and a vocabulary tile dropped from the log-sum-exp (32 rows: about -2e-4; a
+# 128-row slice: about -8.4e-4 at vocab 151936) fails it; test_oracle_scoring.py shows that
+# on the oracle.
+SCORE_TOL = 1e-4
 
 
 class Request:
@@ -153,3 +160,60 @@ def check_argmax(oracle_logits, cand_off, oracle_arg, got_arg):
         else:
             assert got_arg[i] == oracle_arg[i], (i, got_arg[i], oracle_arg[i])
     return ties
+
+
+# The attention launch's work split, restated from the launcher's rule so that tests can put a
+# sample in every unit of work: per KV head, `rows` query rows (real tail token x query head of
+# the group, token-major) are cut into units of 384 rows; when that leaves the last round of
+# workgroups partly empty (or the launch is less than one round), the rows beyond the last full
+# round are re-cut into smaller units, a multiple of 128 rows (one 32-row wave per SIMD), that
+# fill the round. tests/test_unit_plan.py checks this restatement against the launcher itself.
+ROWS_PER_UNIT = 384
+SIMD_ROWS = 128
+
+
+def attention_units(rows, hkv, cus):
+    """[(row0, row_end)] of every unit of one KV head, in unit order."""
+    units = -(-rows // ROWS_PER_UNIT)
+    full, small = units, ROWS_PER_UNIT
+    per_round = cus // hkv
+    if per_round >= 1:
+        if units * hkv <= cus:
+            want = -(-rows // per_round)
+            up = max(SIMD_ROWS, -(-want // SIMD_ROWS) * SIMD_ROWS)
+            if up < ROWS_PER_UNIT:
+                full, small = 0, up
+        else:
+            whole = units // per_round * per_round
+            rem = rows - whole * ROWS_PER_UNIT
+            if rem > 0:
+                s = -(-rem // per_round)
+                s_up = -(-s // SIMD_ROWS) * SIMD_ROWS
+                if s_up < ROWS_PER_UNIT:
+                    full, small = whole, s_up
+    out = []
+    r = 0
+    while r < rows:
+        size = ROWS_PER_UNIT if len(out) < full else small
+        out.append((r, min(rows, r + size)))
+        r += size
+    return out
+
+
+def unit_samples(req, cus):
+    """(question, position, head) at the first and last row of every (unit, KV head) of the
+    attention launch, plus the first and last token of every tail."""
+    cfg = req.cfg
+    g_size = cfg.n_heads_q // cfg.n_heads_kv
+    vs = req.valid_start()
+    picks = set()
+    for i, n in enumerate(req.tail_len):
+        for t in {0, int(n) - 1}:
+            picks.add((i, t, (i * 7 + t) % cfg.n_heads_q))
+    for row0, row_end in attention_units(int(vs[-1]) * g_size, cfg.n_heads_kv, cus):
+        for r in {row0, row_end - 1}:
+            c, hl = divmod(r, g_size)
+            q = int(np.searchsorted(vs, c, side="right") - 1)
+            for g in range(cfg.n_heads_kv):
+                picks.add((q, int(c - vs[q]), g * g_size + hl))
+    return sorted(picks)

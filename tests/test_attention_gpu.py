@@ -2,15 +2,16 @@
 
 Bar: max-abs 2e-2 on the bf16 outputs of every real row. Reduced variants of all five
 workloads run whole against the oracle (several tiles, ragged tails, GQA 4 and 5, with and
-without a prefix); the full-size workloads, launched exactly as the bench launches them, are
-checked on sampled rows. Invariants (padding content, batch composition, head permutation)
+without a prefix); the full-size workloads are launched exactly as the bench launches them and
+checked whole (4B-like, plain max packing) or at the first and last row of every unit of work
+of the launch (long document, 27B-like). Invariants (padding content, batch composition, head permutation)
 must hold bit for bit."""
 
 import numpy as np
 import pytest
 
 import synth
-from helpers import ATTN_TOL, Request, run_attention, sample_rows, valid_rows
+from helpers import ATTN_TOL, Request, run_attention, sample_rows, unit_samples, valid_rows
 from oracle.attention import attention_full, attention_rows
 
 pytestmark = pytest.mark.gpu
@@ -52,13 +53,46 @@ def test_matches_oracle_whole(name):
     assert err <= ATTN_TOL
 
 
-@pytest.mark.parametrize("number", [1, 2, 3, 4, 5])
-def test_full_size_sampled(number):
+def _max_err_by_question(req, got, ref):
+    """Largest |got - ref| over every real row and head, one question at a time."""
+    err = 0.0
+    for i, n in enumerate(req.tail_len):
+        o = int(req.pack["token_offset"][i])
+        part = got[o:o + int(n)]
+        assert np.isfinite(part).all(), f"question {i} has a row that was not written"
+        err = max(err, float(np.abs(part - ref[o:o + int(n)]).max()))
+    return err
+
+
+@pytest.mark.parametrize("number", [2, 4])
+def test_full_size_whole(number):
+    # The 4B-like request (448 workgroups, more than one round) and plain max packing (6392
+    # workgroups, re-cut last round, three packer batches), launched exactly as the bench
+    # launches them, compared with the oracle on every real row and head.
     cfg = synth.config(number)
-    print(f"attention full-size sampled parity: config {number}", flush=True)
+    print(f"attention full-size whole parity: config {number}", flush=True)
     req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
     got = run_attention(req)
-    samples = sample_rows(req, 160 if number != 5 else 96, seed=number)
+    ref = _oracle(req)
+    err = _max_err_by_question(req, got, ref)
+    print(f"  max abs err {err:.3e} over {int(np.sum(req.tail_len))} tokens x "
+          f"{cfg.n_heads_q} heads", flush=True)
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("number", [3, 5])
+def test_full_size_every_unit(number):
+    # The long-document and 27B-like requests are too large for a whole FP64 comparison, so
+    # the oracle checks the first and last row of every unit of work of the launch (each KV
+    # head), the re-cut last-round units included, plus both ends of every tail.
+    import torch
+
+    cfg = synth.config(number)
+    print(f"attention full-size parity at every unit: config {number}", flush=True)
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    got = run_attention(req)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    samples = unit_samples(req, cus)
     ts = req.tensors
     ref = attention_rows(ts["q"], ts["k_tail"], ts["v_tail"], ts.get("k_prefix"),
                          ts.get("v_prefix"), req.pack["token_offset"], req.tail_len,
@@ -66,7 +100,7 @@ def test_full_size_sampled(number):
     off = req.pack["token_offset"]
     picked = np.stack([got[off[i] + t, h] for i, t, h in samples])
     err = np.abs(picked - ref).max()
-    print(f"  max abs err {err:.3e} over {len(samples)} sampled rows", flush=True)
+    print(f"  max abs err {err:.3e} over {len(samples)} rows ({cus} CUs)", flush=True)
     assert np.isfinite(picked).all() and err <= ATTN_TOL
     # every real row was written (the output starts as NaN)
     assert np.isfinite(got[valid_rows(req)]).all()

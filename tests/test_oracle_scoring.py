@@ -1,11 +1,15 @@
 """Pins of the teacher-forced scoring oracle: the pages' row/target positions, closed forms,
-brute force in plain Python on a tiny vocabulary, normalisation and shift invariance."""
+brute force in plain Python on a tiny vocabulary, normalisation and shift invariance; and the
+sensitivity of the GPU bar: a vocabulary tile dropped from the oracle's log-sum-exp moves the
+result by more than the bar the GPU parity tests use."""
 
 import math
 
 import numpy as np
 import pytest
 
+import synth
+from helpers import SCORE_TOL
 from oracle.scoring import ScoringError, score_rows, teacher_forced_logprobs
 
 
@@ -55,3 +59,24 @@ def test_probabilities_sum_to_one_and_shift_invariance():
 def test_refusal():
     with pytest.raises(ScoringError, match="outside the vocabulary"):
         teacher_forced_logprobs(np.zeros((1, 2)), [0], [9], np.zeros((9, 2)))
+
+
+@pytest.mark.parametrize("dropped", [32, 128])
+def test_bar_sees_a_dropped_vocabulary_tile(dropped):
+    # The readout workload's scale (W_U ~ N(0, 0.02) in bf16, hidden ~ N(0, 1)) at the full
+    # vocabulary of 151936, on a narrower hidden width (256) to keep the oracle quick. Dropping
+    # one tile of `dropped` vocabulary rows from the normaliser (a mistake planted in the
+    # oracle's input, on the CPU) must move every log-probability by more than the bar.
+    rng = np.random.default_rng(11)
+    vocab, d = 151936, 256
+    hidden = synth.f32_to_bf16_bits(rng.standard_normal((4, d)).astype(np.float32))
+    w_u = synth.f32_to_bf16_bits((rng.standard_normal((vocab, d)) * 0.02).astype(np.float32))
+    rows, targets = [0, 1, 2, 3], [5, 70000, 150000, 1000]
+    full = teacher_forced_logprobs(hidden, rows, targets, w_u)
+    for start in (256, 66560, vocab - dropped):  # targets lie outside every dropped tile
+        keep = np.ones(vocab, bool)
+        keep[start:start + dropped] = False
+        remap = np.cumsum(keep) - 1
+        cut = teacher_forced_logprobs(hidden, rows, [int(remap[t]) for t in targets], w_u[keep])
+        shift = cut - full
+        assert (shift > SCORE_TOL).all(), (start, shift)

@@ -10,8 +10,9 @@ import pytest
 
 import synth
 from helpers import ATTN_TOL, PROB_TOL, Request, bf16_to_f32_host, check_argmax, device_bf16
-from helpers import valid_rows
-from oracle.attention import attention_full
+from helpers import unit_samples, valid_rows
+from oracle.attention import attention_full, attention_rows
+from oracle.pack import pack_ragged
 from oracle.readout import label_readout
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +57,59 @@ def test_step_matches_oracle(side_stream, readout):
         assert attn_err <= ATTN_TOL
         assert prob_err <= PROB_TOL
         check_argmax(z, req.tables.cand_off, a, arg)
+
+
+@pytest.mark.parametrize("number", [2, 5])
+def test_full_size_step_matches_oracle(number):
+    # One whole step at full size (the bench's step: host pack, table upload, attention,
+    # readout into pinned host memory) against the oracle: the packer's offsets and last rows
+    # bit for bit, the label probabilities and argmax of every question, and attention on
+    # every real row (4B-like) or on the first and last row of every unit of work (27B-like).
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(number)
+    print(f"full-size scoring step: config {number}", flush=True)
+    req = Request(cfg)
+    ts = {k: device_bf16(v) for k, v in req.tensors.items() if v.size}
+    step = blink.ScoringStep(req.tail_len, req.tables.cand_ids, req.tables.cand_off, ts,
+                             cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len, cfg.temperature,
+                             cfg.scale, cfg.token_budget, cfg.max_rows)
+    step.out.fill_(float("nan"))
+    step.h_res.fill_(float("nan"))
+    torch.cuda.synchronize()
+    probs, arg = step.run()
+    pk = pack_ragged(req.tail_len, cfg.token_budget, cfg.max_rows, cfg.prefix_len)
+    assert np.array_equal(step.h_token_offset, pk["token_offset"])
+    assert np.array_equal(step.h_last_row, pk["last_row"])
+    assert np.array_equal(step.h_valid_start, req.valid_start())
+    h = req.tensors
+    z, p, a = label_readout(h["hidden"], pk["last_row"], h["w_u"], req.tables.cand_ids,
+                            req.tables.cand_off, cfg.temperature)
+    prob_err = float(np.abs(probs - p).max())
+    ties = check_argmax(z, req.tables.cand_off, a, arg)
+    out = bf16_to_f32_host(step.out)
+    assert np.isfinite(out[valid_rows(req)]).all()
+    if number == 2:
+        ref = attention_full(h["q"], h["k_tail"], h["v_tail"], h.get("k_prefix"),
+                             h.get("v_prefix"), pk["token_offset"], req.tail_len, cfg.n_heads_q,
+                             cfg.n_heads_kv, cfg.scale)
+        rows = valid_rows(req)
+        attn_err = float(np.abs(out[rows] - ref[rows]).max())
+        what = "every real row"
+    else:
+        samples = unit_samples(req, torch.cuda.get_device_properties(0).multi_processor_count)
+        ref = attention_rows(h["q"], h["k_tail"], h["v_tail"], h.get("k_prefix"),
+                             h.get("v_prefix"), pk["token_offset"], req.tail_len, cfg.n_heads_q,
+                             cfg.n_heads_kv, cfg.scale, samples)
+        got = np.stack([out[pk["token_offset"][i] + t, hd] for i, t, hd in samples])
+        attn_err = float(np.abs(got - ref).max())
+        what = f"{len(samples)} rows at every unit"
+    print(f"  attention err {attn_err:.2e} ({what}), probs err {prob_err:.2e}, "
+          f"{ties} near-ties", flush=True)
+    assert attn_err <= ATTN_TOL
+    assert prob_err <= PROB_TOL
 
 
 def test_typed_answers_from_the_step():

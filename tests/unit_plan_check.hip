@@ -74,7 +74,18 @@ bool check_grouped(const std::vector<int64_t> &rows, int hkv, int cus) {
 
 }  // namespace
 
-int main() {
+int main(int argc, char **argv) {
+  if (argc > 1) {  // "plan": one "rows hkv cus" per input line -> "units full_units small_rows"
+    long long rows = 0;
+    int hkv = 0, cus = 0;
+    while (scanf("%lld %d %d", &rows, &hkv, &cus) == 3) {
+      int64_t full = 0;
+      int small = 0;
+      const int64_t units = unit_split(rows, hkv, cus, full, small);
+      printf("%lld %lld %d\n", (long long)units, (long long)full, small);
+    }
+    return 0;
+  }
   std::mt19937_64 rng(20261202);
   long recut_single = 0, recut_grouped = 0;
   for (int trial = 0; trial < 100000; ++trial) {
