@@ -20,7 +20,9 @@
  *    validation has no effect on device memory.
  *  - The caller owns all memory and the stream. The library allocates no device memory,
  *    keeps no global state between calls and may be called from several threads. The one
- *    call that needs scratch memory (blink_score_targets) takes it from the caller.
+ *    call that needs scratch memory (blink_score_targets) takes it from the caller; its
+ *    variant blink_score_targets_noalloc uses a fixed static scratch array instead (the one
+ *    exception to "no global state", described there).
  *  - Device entry points are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream). Device arrays must stay alive until the work on `stream` has finished.
  *  - bf16 means the 16-bit brain-float storage format. All tensors are dense and row-major
@@ -58,7 +60,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 7
+#define BLINK_ABI_VERSION 8
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -338,6 +340,26 @@ int blink_score_targets(const void *hidden, int64_t hidden_rows, int32_t d_model
                         const int64_t *d_rows, const int32_t *d_targets, int32_t n_rows,
                         const void *w_u, int64_t vocab, float *d_logprob, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * blink_score_targets_noalloc -- device, asynchronous; allocates nothing.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid hipMalloc): blink_score_targets with the same arguments, meaning, layout, error
+ * behaviour and results, minus the workspace. The scratch lives in a static device array of
+ * BLINK_SCORE_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it runs on until the
+ * process ends; its address is looked up once per device (the first call on a device, with
+ * that device current). A call needing more scratch than that, blink_score_targets_workspace
+ * (n_rows, vocab) > BLINK_SCORE_SCRATCH_BYTES (at vocab 151936: more than 1766 scored
+ * rows), returns BLINK_E_LIMIT before anything is launched. Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and give unspecified results. Nothing in the array needs clearing
+ * between calls; each call overwrites what it reads.
+ */
+#define BLINK_SCORE_SCRATCH_BYTES (16u << 20)
+int blink_score_targets_noalloc(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                                const int64_t *d_rows, const int32_t *d_targets, int32_t n_rows,
+                                const void *w_u, int64_t vocab, float *d_logprob, void *stream);
 
 /*
  * blink_combine_rotations -- host, synchronous.

@@ -41,6 +41,7 @@ EXPORTS = (
     "blink_prefix_tail_attention_grouped",
     "blink_score_targets_workspace",
     "blink_score_targets",
+    "blink_score_targets_noalloc",
     "blink_combine_rotations",
     "blink_two_stage_finalists",
 )
@@ -113,6 +114,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.blink_score_targets.restype = ctypes.c_int
     lib.blink_score_targets.argtypes = [_P, _I64, _I32, _P, _P, _I32, _P, _I64, _P, _P,
                                         ctypes.c_size_t, _P]
+    lib.blink_score_targets_noalloc.restype = ctypes.c_int
+    lib.blink_score_targets_noalloc.argtypes = [_P, _I64, _I32, _P, _P, _I32, _P, _I64, _P, _P]
     _PF = ctypes.POINTER(ctypes.c_float)
     lib.blink_combine_rotations.restype = ctypes.c_int
     lib.blink_combine_rotations.argtypes = [_PF, _PI32, _PI32, _PI32, _PF, _I32, _PI32, _I32,
@@ -455,6 +458,13 @@ class TargetScorer:
 
     def run(self):
         _check(self.lib.blink_score_targets(*self.args))
+        return self.logprob
+
+    def run_noalloc(self):
+        """The same scoring through blink_score_targets_noalloc (the library's static scratch
+        instead of this object's workspace)."""
+        a = self.args
+        _check(self.lib.blink_score_targets_noalloc(*a[:9], a[11]))
         return self.logprob
 
 

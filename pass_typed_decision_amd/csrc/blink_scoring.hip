@@ -23,6 +23,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "blink_internal.h"
 
 namespace {
@@ -211,35 +213,62 @@ inline size_t workspace_bytes_for(int64_t n_rows, int64_t vocab) {
   return (part + 255) / 256 * 256 + (size_t(n_rows) * sizeof(float) + 255) / 256 * 256;
 }
 
-}  // namespace
+// Scratch of blink_score_targets_noalloc, for callers that cannot allocate device memory:
+// one copy per GPU the library runs on, held until the process ends. In host code `scratch`
+// names a host-side stand-in, not device memory: its device address on the current GPU comes
+// from hipGetSymbolAddress, taken once per device and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[BLINK_SCORE_SCRATCH_BYTES];
 
-extern "C" size_t blink_score_targets_workspace(int32_t n_rows, int64_t vocab) {
-  if (n_rows < 1 || n_rows > kMaxRows || vocab < 1 || vocab > (int64_t(1) << 31)) return 0;
-  return workspace_bytes_for(n_rows, vocab);
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, resolved on the first call per device.
+int scratch_address(void **out) {
+  using blink::fail;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kMaxDevices)
+    return fail(BLINK_E_DEVICE, "blink_score_targets_noalloc: no usable current device");
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[device]) {
+    void *p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(BLINK_E_DEVICE, "blink_score_targets_noalloc: scratch address on device %d: %s",
+                  device, hipGetErrorString(err));
+    scratch_ptr[device] = p;
+  }
+  *out = scratch_ptr[device];
+  return BLINK_OK;
 }
 
-extern "C" int blink_score_targets(const void *hidden, int64_t hidden_rows, int32_t d_model,
-                                   const int64_t *d_rows, const int32_t *d_targets,
-                                   int32_t n_rows, const void *w_u, int64_t vocab,
-                                   float *d_logprob, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
+// Argument checks shared by both entry points (no device call).
+int check_args(const void *hidden, int64_t hidden_rows, int32_t d_model, const int64_t *d_rows,
+               const int32_t *d_targets, int32_t n_rows, const void *w_u, int64_t vocab,
+               const float *d_logprob) {
   using blink::fail;
-  if (!hidden || !d_rows || !d_targets || !w_u || !d_logprob || !workspace)
+  if (!hidden || !d_rows || !d_targets || !w_u || !d_logprob)
     return fail(BLINK_E_INVALID, "blink_score_targets: a pointer argument is NULL");
   if (n_rows < 1 || n_rows > kMaxRows)
-    return fail(BLINK_E_LIMIT, "%d scored rows; the limit is 1 to %lld", n_rows, (long long)kMaxRows);
+    return fail(BLINK_E_LIMIT, "%d scored rows; the limit is 1 to %lld", n_rows,
+                (long long)kMaxRows);
   if (d_model < kChunk || d_model > kMaxDModel || d_model % kChunk)
     return fail(BLINK_E_INVALID, "d_model %d must be a multiple of %d in %d..%d", d_model,
                 kChunk, kChunk, kMaxDModel);
   if (hidden_rows < 1 || vocab < 1 || vocab > (int64_t(1) << 31))
     return fail(BLINK_E_INVALID, "hidden_rows must be positive and vocab in 1..2^31");
-  if (!blink::aligned16(hidden) || !blink::aligned16(w_u) || !blink::aligned16(workspace))
-    return fail(BLINK_E_INVALID, "hidden, w_u and workspace must be 16-byte aligned");
-  const size_t need = workspace_bytes_for(n_rows, vocab);
-  if (workspace_bytes < need)
-    return fail(BLINK_E_INVALID, "workspace of %zu bytes; %zu needed", workspace_bytes, need);
+  if (!blink::aligned16(hidden) || !blink::aligned16(w_u))
+    return fail(BLINK_E_INVALID, "hidden and w_u must be 16-byte aligned");
+  if (n_slices_of(vocab) > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "vocabulary too large");
+  return BLINK_OK;
+}
+
+// Both kernels on `stream`, with the partials in `workspace` (checked large enough).
+int launch_scoring(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                   const int64_t *d_rows, const int32_t *d_targets, int32_t n_rows,
+                   const void *w_u, int64_t vocab, float *d_logprob, void *workspace,
+                   void *stream) {
   const int64_t slices = n_slices_of(vocab);
-  if (slices > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "vocabulary too large");
   float2 *part = static_cast<float2 *>(workspace);
   const size_t part_bytes = (size_t(slices) * size_t(n_rows) * sizeof(float2) + 255) / 256 * 256;
   float *target_z = reinterpret_cast<float *>(static_cast<char *>(workspace) + part_bytes);
@@ -263,6 +292,52 @@ extern "C" int blink_score_targets(const void *hidden, int64_t hidden_rows, int3
     err = hipGetLastError();
   }
   if (err != hipSuccess)
-    return fail(BLINK_E_DEVICE, "blink_score_targets launch: %s", hipGetErrorString(err));
+    return blink::fail(BLINK_E_DEVICE, "blink_score_targets launch: %s", hipGetErrorString(err));
   return blink::ok();
+}
+
+}  // namespace
+
+extern "C" size_t blink_score_targets_workspace(int32_t n_rows, int64_t vocab) {
+  if (n_rows < 1 || n_rows > kMaxRows || vocab < 1 || vocab > (int64_t(1) << 31)) return 0;
+  return workspace_bytes_for(n_rows, vocab);
+}
+
+extern "C" int blink_score_targets(const void *hidden, int64_t hidden_rows, int32_t d_model,
+                                   const int64_t *d_rows, const int32_t *d_targets,
+                                   int32_t n_rows, const void *w_u, int64_t vocab,
+                                   float *d_logprob, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  using blink::fail;
+  int rc = check_args(hidden, hidden_rows, d_model, d_rows, d_targets, n_rows, w_u, vocab,
+                      d_logprob);
+  if (rc != BLINK_OK) return rc;
+  if (!workspace) return fail(BLINK_E_INVALID, "blink_score_targets: a pointer argument is NULL");
+  if (!blink::aligned16(workspace))
+    return fail(BLINK_E_INVALID, "hidden, w_u and workspace must be 16-byte aligned");
+  const size_t need = workspace_bytes_for(n_rows, vocab);
+  if (workspace_bytes < need)
+    return fail(BLINK_E_INVALID, "workspace of %zu bytes; %zu needed", workspace_bytes, need);
+  return launch_scoring(hidden, hidden_rows, d_model, d_rows, d_targets, n_rows, w_u, vocab,
+                        d_logprob, workspace, stream);
+}
+
+extern "C" int blink_score_targets_noalloc(const void *hidden, int64_t hidden_rows,
+                                           int32_t d_model, const int64_t *d_rows,
+                                           const int32_t *d_targets, int32_t n_rows,
+                                           const void *w_u, int64_t vocab, float *d_logprob,
+                                           void *stream) {
+  using blink::fail;
+  int rc = check_args(hidden, hidden_rows, d_model, d_rows, d_targets, n_rows, w_u, vocab,
+                      d_logprob);
+  if (rc != BLINK_OK) return rc;
+  const size_t need = workspace_bytes_for(n_rows, vocab);
+  if (need > size_t(BLINK_SCORE_SCRATCH_BYTES))
+    return fail(BLINK_E_LIMIT, "%d scored rows over a vocabulary of %lld need %zu bytes of "
+                "scratch; the library's static scratch holds %zu", n_rows, (long long)vocab, need,
+                size_t(BLINK_SCORE_SCRATCH_BYTES));
+  void *ws = nullptr;
+  if ((rc = scratch_address(&ws)) != BLINK_OK) return rc;
+  return launch_scoring(hidden, hidden_rows, d_model, d_rows, d_targets, n_rows, w_u, vocab,
+                        d_logprob, ws, stream);
 }

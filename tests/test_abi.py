@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 7
+    assert blink.load_library().blink_abi_version() == 8
 
 
 def _compare(pk, ref):
@@ -433,6 +433,26 @@ def test_score_targets_refusals_before_launch(blink, kw, code, msg):
     lib = blink.load_library()
     assert _score(lib, **kw) == code
     assert msg in lib.blink_last_error().decode()
+
+
+@pytest.mark.parametrize("kw, code, msg", [
+    (dict(n=1767, vocab=151936), -2, "the library's static scratch holds 16777216"),
+    (dict(n=0), -2, "0 scored rows"),
+    (dict(d_model=100), -1, "d_model 100 must be a multiple of 64"),
+    (dict(null=True), -1, "a pointer argument is NULL"),
+])
+def test_score_targets_noalloc_refusals_before_launch(blink, kw, code, msg):
+    # The no-allocation form refuses sizes beyond its static scratch before any device call.
+    lib = blink.load_library()
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    n, d_model, vocab = kw.get("n", 4), kw.get("d_model", 128), kw.get("vocab", 1000)
+    assert lib.blink_score_targets_noalloc(fake, 10, d_model, fake, fake, n,
+                                           None if kw.get("null") else fake, vocab, fake,
+                                           None) == code
+    assert msg in lib.blink_last_error().decode()
+    # The largest call that fits: at vocab 151936, 1766 rows need exactly 16 MiB.
+    assert lib.blink_score_targets_workspace(1766, 151936) <= 16 << 20
+    assert lib.blink_score_targets_workspace(1767, 151936) > 16 << 20
 
 
 def test_combine_rotations_matches_oracle_random(blink):
