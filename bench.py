@@ -303,6 +303,83 @@ def grouped_attention(cfg, n_req: int, stream, reps: int = 10) -> dict:
             "work_per_launch": f"{flops:.4e} FLOP"}
 
 
+def grouped_step(number: int, n_req: int, stream, steps: int = 20, warmup: int = 3) -> dict:
+    """R requests of the numbered workload's shape (seeds 1000 + workload + 100 r), each with
+    its own prefix, scored together by one GroupedScoringStep (one grouped attention launch and
+    one readout), against the same R requests scored one ScoringStep after another. Both loops
+    synchronise every step and bring the results to the host."""
+    import torch
+
+    import pass_typed_decision_amd as blink
+    import synth
+
+    cfg = synth.config(number)
+    parts = ("q", "k_tail", "v_tail", "k_prefix", "v_prefix", "hidden")
+    reqs, host, base, pstart = [], {k: [] for k in parts}, 0, 0
+    for r in range(n_req):
+        rng = synth.rng_for(cfg, seed=1000 + cfg.number + 100 * r)
+        tables = synth.draw_tables(cfg, rng)
+        pk = blink.pack_ragged(tables.tail_len, cfg.prefix_len, cfg.token_budget, cfg.max_rows)
+        t = synth.draw_tensors(cfg, rng, pk.total_padded_tokens, parts)
+        for k in parts:
+            host[k].append(t[k])
+        reqs.append((tables, pk, base, pstart))
+        base += pk.total_padded_tokens
+        pstart += cfg.prefix_len
+    w_rng = np.random.Generator(np.random.PCG64(5000 + cfg.number))
+    w_u = synth.f32_to_bf16_bits(
+        (w_rng.standard_normal((cfg.vocab, cfg.d_model), dtype=np.float32) * cfg.w_u_std))
+    dev = {k: _dev(np.concatenate(v)) for k, v in host.items() if sum(x.size for x in v)}
+    dev["w_u"] = _dev(w_u)
+    del host, w_u
+    group = blink.GroupedScoringStep(
+        [blink.GroupRequest(tb.tail_len, tb.cand_ids, tb.cand_off, b, ps, cfg.prefix_len)
+         for tb, _, b, ps in reqs], dev, cfg.n_heads_q, cfg.n_heads_kv, cfg.temperature,
+        cfg.scale, cfg.token_budget, cfg.max_rows, stream=stream)
+    singles = []
+    for tb, pk, b, ps in reqs:
+        t = {k: dev[k][b:b + pk.total_padded_tokens] for k in ("q", "k_tail", "v_tail", "hidden")}
+        if cfg.prefix_len:
+            t["k_prefix"] = dev["k_prefix"][ps:ps + cfg.prefix_len]
+            t["v_prefix"] = dev["v_prefix"][ps:ps + cfg.prefix_len]
+        t["w_u"] = dev["w_u"]
+        singles.append(blink.ScoringStep(tb.tail_len, tb.cand_ids, tb.cand_off, t,
+                                         cfg.n_heads_q, cfg.n_heads_kv, cfg.prefix_len,
+                                         cfg.temperature, cfg.scale, cfg.token_budget,
+                                         cfg.max_rows, stream=stream))
+    for _ in range(warmup):
+        group.run()
+        for st in singles:
+            st.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        res = group.run()
+    t_group = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for st in singles:
+            st.run()
+    t_single = time.perf_counter() - t0
+    # The group gives each request exactly its single-request probabilities.
+    for st, (probs, arg) in zip(singles, res):
+        p1, a1 = st.run()
+        if not (np.array_equal(np.concatenate(probs), p1) and np.array_equal(arg, a1)):
+            raise RuntimeError("grouped step differs from single-request steps")
+    n_q = sum(len(tb.tail_len) for tb, _, _, _ in reqs)
+    for st in singles:
+        st.close()
+    del group, singles, dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": f"{n_req} requests of {cfg.name} (config {cfg.number}), each with its "
+                        f"own {cfg.prefix_len}-token prefix", "questions": n_q,
+            "grouped_questions_per_s": n_q * steps / t_group,
+            "grouped_ms_per_step": t_group * 1e3 / steps,
+            "one_step_per_request_questions_per_s": n_q * steps / t_single,
+            "speedup": t_single / t_group, "checked_equal_to_single_requests": True}
+
+
 def teacher_forced_scoring(cfg, tables, pk, tensors, stream, score_len: int = 8,
                            reps: int = 10) -> dict:
     """The request's questions scored teacher-forced on their last score_len tokens: the rows
@@ -495,6 +572,9 @@ def main():
     ap.add_argument("--group", type=int, default=0, metavar="R",
                     help="also time R requests of the workload's shape, each with its own "
                          "prefix, in one grouped attention launch")
+    ap.add_argument("--group-step", default="2:8", metavar="N:R",
+                    help="also score R requests of workload N, each with its own prefix, in one "
+                         "grouped step (empty for none)")
     ap.add_argument("--readout", default="per_option", choices=("per_option", "batched"),
                     help="readout form: per option (default), or batched over the distinct "
                          "label rows")
@@ -597,6 +677,11 @@ def main():
         if number != cfg.number:
             others[synth_name(number)] = secondary(number, stream, readout=args.readout)
 
+    group_step = None
+    if args.group_step:
+        g_num, g_req = (int(x) for x in args.group_step.split(":"))
+        group_step = grouped_step(g_num, g_req, stream)
+
     refs = library_references(stream)
     roof["frac_of_library_reference"] = roof["achieved"] / (
         refs["bf16_gemm_tflops"] if roof["bound"] == "mfma" else refs["hbm_read_gbps"])
@@ -657,6 +742,7 @@ def main():
         "secondary": others,
         "prefix_encode_once_per_request": prefix,
         "grouped_requests": grouped,
+        "grouped_step": group_step,
         "teacher_forced_scoring": scoring,
         "library_references": refs,
         "cpu_baseline": baseline,

@@ -8,7 +8,8 @@ Three calls, each a thin binding of the C ABI in ``include/blink.h`` (libblink.s
 * ``label_readout``          -- HIP kernel: last-real-row gather, FP32 dot with the offered
                                 labels' unembedding rows, temperature softmax, argmax.
 
-``score`` chains them for one request (the hot path of one scoring step).
+``ScoringStep`` chains them for one request (the hot path of one scoring step);
+``GroupedScoringStep`` runs several requests, each with its own prefix, in one pass.
 """
 
 from ._binding import (
@@ -46,6 +47,7 @@ from ._binding import (
     two_stage_finalists,
     prefix_tail_attention,
 )
+from .group import GroupRequest, GroupedScoringStep
 from .path import ScoringStep, label_name
 
 __all__ = [
@@ -83,5 +85,7 @@ __all__ = [
     "pack_ragged",
     "prefix_tail_attention",
     "ScoringStep",
+    "GroupRequest",
+    "GroupedScoringStep",
     "label_name",
 ]

@@ -76,6 +76,7 @@
 
 #include "blink_internal.h"
 
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -292,7 +293,15 @@ __device__ inline void issue_load(const TileRsrc &r, char *lds_k, char *lds_v, i
   const int inst = wave + kWaves * i;  // uniform
   const bool is_k = inst < L::KINST;
   char *dst = is_k ? lds_k + inst * 1024 : lds_v + (inst - L::KINST) * 1024;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? r.k : r.v, dst, 16, plan.voff[i], 0, 0, 0);
+  // The load is written in asm so that the compiler does not track it: tracked, it makes every
+  // later LDS read of the wave (the V transpose reads of the tile being computed) wait for this
+  // load, which only the next pair of tiles needs. The loads carry no output registers; the
+  // explicit wait and barrier at the end of each pair (wait_tile_loads) publish them. The
+  // s_nop keeps one wait state between the write of m0 and the load that reads it.
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_char *)dst));
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(plan.voff[i]), "s"(is_k ? r.k : r.v), "{m0}"(lds));
 }
 
 // All of this wave's loads of one tile.
