@@ -36,27 +36,26 @@
 //    Each lane of a direct load computes which (row, 16-byte chunk) its fixed LDS slot holds;
 //    pad slots load out of range and receive zeros.
 //  * Softmax in FP32 on exp2. Q is pre-scaled by scale * log2(e) (rounded to bf16 once, as a
-//    standard bf16 attention does). Each row's reference m is the max of the first tile it
-//    sees; later tiles enter the S accumulator with -m as its initial value, so exp2 reads the
-//    accumulator directly, and probabilities may grow up to 2^64 above the reference (FP32
-//    and bf16 hold that with room to spare), so the O accumulators are never rescaled inside
-//    the loop. Should any row's scores exceed its reference by more than that (extreme
-//    inputs only), its sum of probabilities ends above 2^64 (or inf or NaN), which one check
-//    per row at the end of the unit catches (the full-tile path itself takes no row maxima),
-//    and the workgroup recomputes exactly: one pass for the exact row maxima, then the normal
-//    pass with m fixed at them. Row sums are taken over the bf16-rounded
-//    probabilities that the PV product uses (v_dot2 with ones). Nothing a row computes depends
-//    on which other rows share its wave.
+//    standard bf16 attention does). The main pass gives every row the fixed reference 0: a
+//    probability is exp2 of the raw score, so the score chains start from the MFMA's zero
+//    accumulator input, no row maximum is taken and the O accumulators are never rescaled.
+//    Softmax is invariant under the reference, and FP32 and bf16 keep full relative precision
+//    while each row's sum of probabilities stays within 2^-64 .. 2^64; one check per row at the
+//    end of the unit catches a row outside it (or an inf or NaN: scores beyond the range of
+//    exp2, or all far below 0; extreme inputs only), and the workgroup recomputes exactly: one
+//    pass for the exact row maxima, then the normal pass with m fixed at them. Row sums are
+//    taken over the bf16-rounded probabilities that the PV product uses (v_dot2 with ones).
+//    Nothing a row computes depends on which other rows share its wave.
 //  * Prefix tiles first (unmasked except the last partial tile), then the tail tiles of each
 //    question the unit touches, masked per lane (same question and key <= position).
-//  * Two tile paths. Whole tiles for a wave whose rows all have their reference take a
-//    branch-free path with no row maxima: both 32-key score blocks, then exp2, bf16, row sums
-//    and PV, with the next tiles' loads issued between the score MFMAs, which run at raised
-//    wave priority so the matrix pipe is fed ahead of other waves' softmax. A whole tile is a
-//    full prefix tile, or a tail tile of the wave's one question whose 64 keys all lie at or
-//    before every row of the wave (in a long causal tail, such as the prefix's own prefill,
-//    nearly all of them). Everything else (tiles that cut the causal diagonal, the last partial
-//    prefix tile, a row's first tile) takes the general path, one 32-key block at a time.
+//  * Two tile paths. Whole tiles of the main pass take a branch-free path: both 32-key score
+//    blocks, then exp2, bf16, row sums and PV, with the next tiles' loads issued between the
+//    score MFMAs, which run at raised wave priority so the matrix pipe is fed ahead of other
+//    waves' softmax. A whole tile is a full prefix tile, or a tail tile of the wave's one
+//    question whose 64 keys all lie at or before every row of the wave (in a long causal tail,
+//    such as the prefix's own prefill, nearly all of them). Everything else (tiles that cut the
+//    causal diagonal, the last partial prefix tile, every tile of the exact recomputation)
+//    takes the general path, one 32-key block at a time.
 //  * The request's row tables (valid_start, token_offset) are copied into LDS when the
 //    workgroup starts, so every lookup on the way to the first tile is an LDS read.
 //  * Output rows go through LDS (two idle stages of the ring, half a row at a time) so that
@@ -98,9 +97,11 @@ constexpr int kStages = 4;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxRequests = BLINK_MAX_REQUESTS;  // prefixes in one grouped launch
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kHeadroom = 64.0f;              // log2 units a score may exceed its reference
+constexpr float kHeadroom = 64.0f;              // log2 units a row sum may lie from 1
 constexpr float kSumLimit = 0x1p64f;            // 2^kHeadroom: largest row sum a pass accepts
-static_assert(kSumLimit == 0x1p64f && kHeadroom == 64.0f, "the row-sum check is 2^kHeadroom");
+constexpr float kSumFloor = 0x1p-64f;           // 2^-kHeadroom: smallest row sum a pass accepts
+static_assert(kSumLimit == 0x1p64f && kSumFloor == 0x1p-64f && kHeadroom == 64.0f,
+              "the row-sum check is 2^-kHeadroom .. 2^kHeadroom");
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3 (32-bit data)
 constexpr int kWaitFlags = 0xF70;               // s_waitcnt with expcnt/lgkmcnt at their max
 
@@ -169,7 +170,7 @@ struct Smem {
   __attribute__((aligned(16))) char k[kStages][Layout<D>::KBYTES];
   __attribute__((aligned(16))) char v[kStages][Layout<D>::VBYTES];
   Tables tab;
-  int overflow;  // some row of the workgroup ended with a sum of probabilities above 2^kHeadroom
+  int overflow;  // some row of the workgroup ended with a sum of probabilities out of range
 };
 
 // Waits until this wave's tile loads have all landed. They are the only vector memory
@@ -374,17 +375,20 @@ __device__ inline void pv_product(const char *vt, int key0, const bf16x8 (&pb)[k
 
 // kt/vt point at the tile plus this lane's part of the fragment addresses.
 // MAX_ONLY: only the row maxima are taken (raw scores, log2 units) for the exact pass.
-template <int D, bool MAX_ONLY>
+// ZERO: every row's reference is 0 (the main pass): the score chain starts from the MFMA's zero
+// accumulator input; otherwise it starts from -m.
+template <int D, bool MAX_ONLY, bool ZERO>
 __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
                                        bf16x8 (&qf)[kQB][D / 16],
                                        f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB],
                                        bool masked, const int (&lim)[kQB]) {
   f32x16 s[kQB];
+  if (!(MAX_ONLY || ZERO)) {
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float init = (MAX_ONLY || rs[qb].m == -INFINITY) ? 0.0f : -rs[qb].m;
+    for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[qb][v] = init;
+      for (int v = 0; v < 16; ++v) s[qb][v] = -rs[qb].m;
+    }
   }
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -392,7 +396,8 @@ __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
         *reinterpret_cast<const u32x4 *>(kt + key0 * Layout<D>::KRS + ks * 32));
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          kf, qf[qb][ks], (ks == 0 && (MAX_ONLY || ZERO)) ? f32x16{} : s[qb], 0, 0, 0);
   }
 
   if (masked) {  // uniform: tail tiles and the last partial prefix tile
@@ -415,37 +420,20 @@ __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
     }
     return;
   }
-  // Row maxima are needed only to set the reference of rows that have none yet (a score far
-  // above a reference shows up in the row sum, which the kernel checks at the end).
-  bool no_ref = false;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) no_ref |= rs[qb].m == -INFINITY;
+  // No row maxima: every row's reference is fixed for the pass (0, or its exact maximum in the
+  // recomputation), and a row sum out of range is caught at the end of the unit.
   bf16x8 pb[kQB][2];
-  if (__builtin_amdgcn_ballot_w64(no_ref)) {
-    // First visible keys of some row: its reference becomes this tile's max (its O and l
-    // are still zero). Other rows subtract 0, bit-identical to the common path.
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float m = s[qb][0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[qb][v]);
-      const float mx = pair_max(m);
-      const bool fresh = rs[qb].m == -INFINITY && mx > -INFINITY;
-      const float delta = fresh ? mx : 0.0f;
-      if (fresh) rs[qb].m = mx;
-      probs_to_bf16(s[qb], delta, pb[qb], rs[qb].l);
-    }
-  } else {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[qb], 0.0f, pb[qb], rs[qb].l);
-  }
+  for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[qb], 0.0f, pb[qb], rs[qb].l);
   pv_product<D>(vt, key0, pb, o);
 }
 
-// A full, unmasked 64-key tile for a wave whose rows all have their reference already (the
-// common case: every prefix tile after the first). Both 32-key score blocks are computed
-// first, all in one basic block, so one block's softmax (vector ALU) can be interleaved with
-// the other block's matrix products.
+// A full, unmasked 64-key tile in the main pass, where every row's reference is 0: the score
+// chains start from the MFMA's zero accumulator input, so no vector instruction sets them up (on
+// this chip the matrix pipe and the vector ALU share each SIMD's issue, so vector instructions
+// taken out of the tile are time taken out of it). Both 32-key score blocks are computed first,
+// all in one basic block, so one block's softmax (vector ALU) can be interleaved with the other
+// block's matrix products.
 // The next tile's FULL regular loads are issued between the score MFMAs, one per 4 MFMAs, so
 // the waves of a CU do not all queue their loads at once after the barrier.
 template <int D>
@@ -461,14 +449,6 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
   __builtin_amdgcn_s_setprio(1);
   f32x16 s[2][kQB];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float init = -rs[qb].m;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[sub][qb][v] = init;
-    }
-#pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -476,7 +456,8 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
           *reinterpret_cast<const u32x4 *>(kt + 32 * sub * Layout<D>::KRS + ks * 32));
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
-        s[sub][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[sub][qb], 0, 0, 0);
+        s[sub][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kf, qf[qb][ks], ks == 0 ? f32x16{} : s[sub][qb], 0, 0, 0);
       const int step = sub * (D / 16) + ks;
       if (step % 4 == 3 && step / 4 < Layout<D>::FULL)
         issue_load<D>(load_src, next_k, next_v, wave, plan, step / 4);
@@ -491,8 +472,8 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
     if (step % 4 == 3 && step / 4 < Layout<D>::FULL)
       __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
   }
-  // No row maximum here: a probability above 2^kHeadroom shows up in the row sum, which the
-  // kernel checks once at the end of the unit.
+  // No row maximum here: a row whose probabilities leave the representable range shows up in
+  // its row sum, which the kernel checks once at the end of the unit.
   bf16x8 pb[2][kQB][2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
@@ -559,13 +540,15 @@ struct WaveSpan {
 };
 
 template <int D>
-__device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], bool reset_m) {
+// Clears the accumulators; `m`: the rows' reference for the pass (0 for the main pass, -inf
+// before the exact maxima are taken), or NaN to keep the references as they are.
+__device__ inline void init_rows(f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], float m) {
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[qb][db] = f32x16{};
     rs[qb].l = 0.f;
-    if (reset_m) rs[qb].m = -INFINITY;
+    if (!isnan(m)) rs[qb].m = m;
   }
 }
 
@@ -588,7 +571,7 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
                                  int klane, int vlane, int wave, int lane,
                                  const LoadPlan<D> &plan, bf16x8 (&qf)[kQB][D / 16],
                                  f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB], bool max_only,
-                                 bool started) {
+                                 bool zero_ref, bool started) {
   const int half = lane >> 5;
   // Tiles go in pairs (2t, 2t + 1) -> stages (0, 1) or (2, 3). While a pair is computed, the
   // next pair is loaded into the other two stages; one wait for all loads plus one barrier at
@@ -614,14 +597,11 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     if (cur.q >= 0)
       active = active && cur.q >= ws.qa && cur.q <= ws.qz &&
                !(cur.q == ws.qz && cur.kstart > ws.posz);
-    bool fresh = false;  // some row of this wave has not seen a visible key yet
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) fresh |= rs[qb].m == -INFINITY;
     // A whole tile: every key visible to every row of the wave (see the two tile paths).
     const bool whole = cur.q < 0 ? cur.kstart + kTileKeys <= cur.klimit
                                  : cur.q == ws.qa && ws.qa == ws.qz &&
                                        cur.kstart + kTileKeys <= ws.posa + 1;
-    const bool fast = !max_only && whole && !__builtin_amdgcn_ballot_w64(fresh);
+    const bool fast = !max_only && zero_ref && whole;
     if (active && fast) {
       compute_tile_fast<D>(sm.k[stage] + klane, sm.v[stage] + vlane, qf, o, rs, ra,
                            sm.k[stage2], sm.v[stage2], wave, plan);
@@ -650,9 +630,11 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
           lim[qb] = last - 4 * half;
         }
         if (max_only)
-          compute_subtile<D, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+          compute_subtile<D, true, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+        else if (zero_ref)
+          compute_subtile<D, false, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
         else
-          compute_subtile<D, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+          compute_subtile<D, false, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
       }
     }
 
@@ -867,13 +849,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const WaveSpan ws{wave_active, wqa, wqz, wposz, wposa};
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
-  init_rows<D>(o, rs, true);
+  init_rows<D>(o, rs, 0.0f);
   run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
-               true);
-  // Any probability above 2^kHeadroom (or an inf or NaN) leaves its row sum above 2^kHeadroom.
+               true, true);
+  // A probability above 2^kHeadroom (or an inf or NaN) leaves its row sum above 2^kHeadroom; a
+  // row whose scores all lie far below 0 leaves it below 2^-kHeadroom.
   bool over = false;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) over |= rvalid[qb] && !(pair_sum(rs[qb].l) <= kSumLimit);
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float l = pair_sum(rs[qb].l);
+    over |= rvalid[qb] && !(l <= kSumLimit && l >= kSumFloor);
+  }
   store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
   // Did any wave of the workgroup overflow? (The flag was cleared before the first barrier.)
   // The barrier orders only the flag in LDS, so the workgroup does not wait for its stores to
@@ -884,12 +870,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     // Extreme inputs only: exact row maxima first, then the normal pass with those references;
     // its rows overwrite the ones just stored. (The accumulators are reused: the stored values
     // are dead, so nothing has to be merged.)
-    init_rows<D>(o, rs, true);
+    init_rows<D>(o, rs, -INFINITY);
     run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, true,
-                 false);
-    init_rows<D>(o, rs, false);
+                 false, false);
+    init_rows<D>(o, rs, __builtin_nanf(""));
     run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
-                 false);
+                 false, false);
     store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
   }
 #endif
