@@ -19,10 +19,11 @@
  *  - Every argument error is detected before anything is launched; a call that fails
  *    validation has no effect on device memory.
  *  - The caller owns all memory and the stream. The library allocates no device memory,
- *    keeps no global state between calls and may be called from several threads. The one
- *    call that needs scratch memory (blink_score_targets) takes it from the caller; its
- *    variant blink_score_targets_noalloc uses a fixed static scratch array instead (the one
- *    exception to "no global state", described there).
+ *    keeps no global state between calls and may be called from several threads. Calls that
+ *    need scratch memory take it from the caller as a workspace (blink_score_targets, and
+ *    blink_prefix_tail_attention where its work split uses one); the variant
+ *    blink_score_targets_noalloc uses a fixed static scratch array instead (the one exception
+ *    to "no global state", described there).
  *  - Device entry points are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream). Device arrays must stay alive until the work on `stream` has finished.
  *  - bf16 means the 16-bit brain-float storage format. All tensors are dense and row-major
@@ -60,7 +61,7 @@ const char *blink_last_error(void);
 
 /* ABI version of this header (incremented on any signature change). */
 int blink_abi_version(void);
-#define BLINK_ABI_VERSION 8
+#define BLINK_ABI_VERSION 9
 
 /*
  * blink_pack_ragged -- host, synchronous, integer only.
@@ -166,8 +167,9 @@ int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, int32_t n_s
  * over the P prefix keys of KV head g = h / (H_q / H_kv) followed by the question's own tail
  * keys 0..t (tok = token_offset[i] + t). This equals plain causal attention over the full
  * sequence [prefix ; tail_i] at positions P..P+n_i-1; only the floating-point order differs.
- * Inputs are post-rotary; no positional encoding is applied. Softmax and accumulation are
- * FP32; QK^T and PV use bf16 matrix cores; out is rounded to bf16 (nearest even).
+ * Inputs are post-rotary; no positional encoding is applied. QK^T and PV use bf16 matrix cores
+ * on the inputs as given; the scale multiplies the FP32 scores; softmax and accumulation are
+ * FP32; out is rounded to bf16 (nearest even).
  *
  *   q        bf16 [T_pad, H_q, D]     device
  *   k_tail, v_tail  bf16 [T_pad, H_kv, D]   device
@@ -182,8 +184,20 @@ int blink_plan_prefix(const int32_t *tokens, const int64_t *seq_off, int32_t n_s
  *   n_heads_q, n_heads_kv  H_kv >= 1, H_q % H_kv == 0, H_q / H_kv <= 16
  *   head_dim          64 or 128
  *   scale             finite, > 0 (1/sqrt(D) for standard attention)
- * Rows of one question never depend on which other questions share the launch (results are
- * bitwise identical whether a question runs alone or packed with others).
+ *   workspace, workspace_bytes  optional device scratch (16-byte aligned; NULL / 0 for none),
+ *                     owned by the caller, contents not preserved. When a request's query rows
+ *                     need more than one round of the device's compute units and leave the
+ *                     last round part-empty, the launch can split that round's units by prefix
+ *                     keys (their partial sums go through the workspace and a merge pass adds
+ *                     them); it does so when workspace_bytes is at least
+ *                     blink_prefix_tail_attention_workspace(...) for the same sizes on the
+ *                     current device, and otherwise cuts that round into smaller row units.
+ *                     Either way the result is the same attention (rounding aside). Calls that
+ *                     share one workspace on different streams race.
+ * Without a workspace, rows of one question never depend on which other questions share the
+ * launch: results are bitwise identical whether a question runs alone or packed with others.
+ * With one, rows that fall in key-split units are summed in another order and agree with
+ * those results up to rounding.
  */
 int blink_prefix_tail_attention(const void *q, const void *k_tail, const void *v_tail,
                                 const void *k_prefix, const void *v_prefix, void *out,
@@ -191,7 +205,14 @@ int blink_prefix_tail_attention(const void *q, const void *k_tail, const void *v
                                 int32_t n_questions, int64_t total_valid_tokens,
                                 int64_t total_padded_tokens, int32_t prefix_len,
                                 int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
-                                float scale, void *stream);
+                                float scale, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Workspace bytes blink_prefix_tail_attention uses for these sizes on the current device
+ * (0: its work split needs none; also 0 for sizes it would refuse). */
+size_t blink_prefix_tail_attention_workspace(int64_t total_valid_tokens, int32_t n_heads_q,
+                                             int32_t n_heads_kv, int32_t head_dim,
+                                             int32_t prefix_len);
 
 /*
  * blink_prefix_tail_attention_grouped -- device, asynchronous.

@@ -45,6 +45,7 @@ from ._binding import (
     pack_ragged,
     plan_prefix,
     two_stage_finalists,
+    attention_workspace,
     prefix_tail_attention,
 )
 from .group import GroupRequest, GroupedScoringStep
@@ -83,6 +84,7 @@ __all__ = [
     "load_library",
     "pack_labels",
     "pack_ragged",
+    "attention_workspace",
     "prefix_tail_attention",
     "ScoringStep",
     "GroupRequest",

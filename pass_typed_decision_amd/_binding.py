@@ -33,6 +33,7 @@ EXPORTS = (
     "blink_abi_version",
     "blink_pack_ragged",
     "blink_prefix_tail_attention",
+    "blink_prefix_tail_attention_workspace",
     "blink_label_readout",
     "blink_pack_labels",
     "blink_label_readout_batched",
@@ -88,7 +89,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.blink_prefix_tail_attention.restype = ctypes.c_int
     lib.blink_prefix_tail_attention.argtypes = [
         _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _F32, _P,
+        ctypes.c_size_t, _P,
     ]
+    lib.blink_prefix_tail_attention_workspace.restype = ctypes.c_size_t
+    lib.blink_prefix_tail_attention_workspace.argtypes = [_I64, _I32, _I32, _I32, _I32]
     lib.blink_label_readout.restype = ctypes.c_int
     lib.blink_label_readout.argtypes = [
         _P, _I64, _I32, _P, _P, _I64, _P, _P, _I32, _I64, _I32, _F32, _P, _P, _P, _P,
@@ -295,14 +299,35 @@ def _dev_or_pinned(t, dtype, name):
     return _dev(t, dtype, name)
 
 
+class _ArgList(list):
+    """A checked argument list that also holds the device memory its addresses point into."""
+
+    keep = None
+
+
+def attention_workspace(total_valid_tokens: int, n_heads_q: int, n_heads_kv: int,
+                        head_dim: int, prefix_len: int, device=None):
+    """Device workspace for blink_prefix_tail_attention at these sizes on the current device
+    (a uint8 tensor), or None when its work split needs none."""
+    import torch
+
+    size = int(load_library().blink_prefix_tail_attention_workspace(
+        int(total_valid_tokens), int(n_heads_q), int(n_heads_kv), int(head_dim), int(prefix_len)))
+    if size == 0:
+        return None
+    return torch.empty(size, dtype=torch.uint8, device=device)
+
+
 def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offset,
                           valid_start, total_valid_tokens: int, scale: float, stream=None,
-                          launch: bool = True):
+                          launch: bool = True, workspace="auto"):
     """Launches blink_prefix_tail_attention. Shapes: q/out [T_pad, H_q, D], k/v_tail
     [T_pad, H_kv, D], k/v_prefix [P, H_kv, D] or None; token_offset int64 [n],
-    valid_start int32 [n + 1] (device). With ``launch=False`` returns the checked argument
-    list instead (index 9 is total_valid_tokens) for repeated launches; it holds raw
-    addresses, so the caller keeps every tensor alive while the list is in use."""
+    valid_start int32 [n + 1] (device). ``workspace``: "auto" allocates what the library asks
+    for on the current device (on the launch stream's order), None passes none, or a uint8
+    device tensor. With ``launch=False`` returns the checked argument list instead (index 9 is
+    total_valid_tokens) for repeated launches; it holds raw addresses, so the caller keeps every
+    tensor alive while the list is in use (the list itself holds an automatic workspace)."""
     import torch
 
     bf = torch.bfloat16
@@ -325,11 +350,30 @@ def prefix_tail_attention(q, k_tail, v_tail, k_prefix, v_prefix, out, token_offs
     if int(valid_start.shape[0]) != n + 1:
         raise BlinkError(BLINK_E_INVALID, "valid_start must have n + 1 entries")
     lib = load_library()
-    args = [
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise BlinkError(BLINK_E_INVALID, "workspace must be 'auto', None or a tensor")
+        if stream is not None and launch:
+            # the allocator orders reuse on the current stream; the launch runs on `stream`
+            torch.cuda.ExternalStream(int(stream)).wait_stream(torch.cuda.current_stream())
+        workspace = attention_workspace(int(total_valid_tokens), int(hq), int(hkv), int(d), p,
+                                        device=q.device)
+        if workspace is not None and stream is not None and launch:
+            workspace.record_stream(torch.cuda.ExternalStream(int(stream)))
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+            raise BlinkError(BLINK_E_INVALID, "workspace must be a device tensor")
+        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * \
+            workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    args = _ArgList([
         _dev(q, bf, "q"), _dev(k_tail, bf, "k_tail"), _dev(v_tail, bf, "v_tail"), kp, vp,
         _dev(out, bf, "out"), _dev(token_offset, torch.int64, "token_offset"),
         _dev(valid_start, torch.int32, "valid_start"), n, int(total_valid_tokens), int(t_pad),
-        p, int(hq), int(hkv), int(d), float(scale), _stream(stream)]
+        p, int(hq), int(hkv), int(d), float(scale), ws_ptr, ctypes.c_size_t(ws_bytes),
+        _stream(stream)])
+    args.keep = workspace
     if not launch:
         return args
     _check(lib.blink_prefix_tail_attention(*args))

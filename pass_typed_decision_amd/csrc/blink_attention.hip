@@ -35,10 +35,13 @@
 //    conflicts, and every fragment address is one base register plus an immediate offset.
 //    Each lane of a direct load computes which (row, 16-byte chunk) its fixed LDS slot holds;
 //    pad slots load out of range and receive zeros.
-//  * Softmax in FP32 on exp2. Q is pre-scaled by scale * log2(e) (rounded to bf16 once, as a
-//    standard bf16 attention does). The main pass gives every row the fixed reference 0: a
-//    probability is exp2 of the raw score, so the score chains start from the MFMA's zero
-//    accumulator input, no row maximum is taken and the O accumulators are never rescaled.
+//  * Softmax in FP32 on exp2. Q enters the score MFMAs as given; the FP32 score q . k is then
+//    multiplied by scale * log2(e), so no rounding beyond the MFMA's own FP32 accumulation comes
+//    before the exponential. (Rounding a pre-scaled Q to bf16 instead would move every score by
+//    up to 2^-9 of |q| |k| relative, enough to shift the weights of keys with large norms by a
+//    few percent.) The main pass gives every row the fixed reference 0: a probability is
+//    exp2(c * q . k), so the score chains start from the MFMA's zero accumulator input, no row
+//    maximum is taken and the O accumulators are never rescaled.
 //    Softmax is invariant under the reference, and FP32 and bf16 keep full relative precision
 //    while each row's sum of probabilities stays within 2^-64 .. 2^64; one check per row at the
 //    end of the unit catches a row outside it (or an inf or NaN: scores beyond the range of
@@ -103,6 +106,7 @@ constexpr float kSumFloor = 0x1p-64f;           // 2^-kHeadroom: smallest row su
 static_assert(kSumLimit == 0x1p64f && kSumFloor == 0x1p-64f && kHeadroom == 64.0f,
               "the row-sum check is 2^-kHeadroom .. 2^kHeadroom");
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3 (32-bit data)
+
 constexpr int kWaitFlags = 0xF70;               // s_waitcnt with expcnt/lgkmcnt at their max
 
 struct Args {
@@ -131,6 +135,19 @@ struct Args {
   // [req_unit[r], req_unit[r+1]) and prefix rows [req_pstart[r], req_pstart[r] + req_plen[r]).
   // Its first req_full[r] units hold kRowsPerUnit rows each, the later ones req_small[r] rows
   // each (see grouped_split).
+  // Key split of a single-request launch (split_ways >= 2): units [split_first, n_units) per
+  // KV head are pieces. Piece p = unit - split_first works on the rows of base unit
+  // b = p / split_ways (kRowsPerUnit rows from split_row0 + b * kRowsPerUnit) over prefix tiles
+  // [(p % split_ways) * split_tiles, + split_tiles); only the last piece of a base unit walks
+  // the tail keys. Pieces write their unnormalised sums to `part` (kPartFloats floats per lane
+  // of each wave, per piece and KV head); the merge pass (merge = 1, one workgroup per base
+  // unit and KV head) adds a base unit's pieces and stores its rows.
+  int64_t split_first;
+  int split_ways;
+  int split_tiles;
+  int64_t split_row0;
+  float *part;
+  int merge;
   int n_req;
   int req_first[kMaxRequests + 1];
   int64_t req_unit[kMaxRequests + 1];
@@ -339,24 +356,27 @@ __device__ inline bf16x8 read_v(const char *vt, int vlane, int key0, int db) {
 }
 
 // Probabilities of one 16-value accumulator slice into bf16 B operands, with row-sum update.
-__device__ inline void probs_to_bf16(const f32x16 &s, float delta, bf16x8 (&pb)[2], float &l) {
+// Probabilities of 16 raw scores (q . k, FP32): p = exp2(s * c - m), c = scale * log2(e) and m
+// the row's reference in log2 units (0 for ZERO), rounded to bf16 for the PV product; their sum
+// is added into l.
+template <bool ZERO>
+__device__ inline void probs_to_bf16(const f32x16 &s, float c, float m, bf16x8 (&pb)[2],
+                                     float &l) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto arg = [&](float x) { return ZERO ? x * c : __builtin_fmaf(x, c, -m); };
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(s[8 * c + e] - delta),
-                         (__bf16)__builtin_amdgcn_exp2f(s[8 * c + e + 1] - delta)};
-      pb[c][e] = p2[0];
-      pb[c][e + 1] = p2[1];
+      const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(arg(s[8 * h + e])),
+                         (__bf16)__builtin_amdgcn_exp2f(arg(s[8 * h + e + 1]))};
+      pb[h][e] = p2[0];
+      pb[h][e + 1] = p2[1];
       l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
     }
   }
 }
 
-// One 32-key sub-tile for one wave: S'^T = K Q'^T - m, online softmax, O^T += V^T P^T.
-// lim[qb]: largest visible key index within the sub-tile minus 4 * (lane >> 5); keys above it
-// are masked (used only when MASKED).
 // O^T += V^T P^T over one 32-key sub-tile (two 16-key MFMA steps per 32-dim block).
 template <int D>
 __device__ inline void pv_product(const char *vt, int key0, const bf16x8 (&pb)[kQB][2],
@@ -373,23 +393,19 @@ __device__ inline void pv_product(const char *vt, int key0, const bf16x8 (&pb)[k
   }
 }
 
-// kt/vt point at the tile plus this lane's part of the fragment addresses.
-// MAX_ONLY: only the row maxima are taken (raw scores, log2 units) for the exact pass.
-// ZERO: every row's reference is 0 (the main pass): the score chain starts from the MFMA's zero
-// accumulator input; otherwise it starts from -m.
+// One 32-key sub-tile for one wave: S^T = K Q^T, softmax terms, O^T += V^T P^T.
+// kt/vt point at the tile plus this lane's part of the fragment addresses; c = scale * log2(e).
+// lim[qb]: largest visible key index within the sub-tile minus 4 * (lane >> 5); keys above it
+// are masked (used only when `masked`).
+// MAX_ONLY: only the row maxima are taken (scores times c, log2 units) for the exact pass.
+// ZERO: every row's reference is 0 (the main pass); otherwise each row's reference is its m.
+// The score chains start from the MFMA's zero accumulator input either way.
 template <int D, bool MAX_ONLY, bool ZERO>
 __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
                                        bf16x8 (&qf)[kQB][D / 16],
                                        f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB],
-                                       bool masked, const int (&lim)[kQB]) {
+                                       bool masked, const int (&lim)[kQB], float c) {
   f32x16 s[kQB];
-  if (!(MAX_ONLY || ZERO)) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[qb][v] = -rs[qb].m;
-    }
-  }
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 kf = as_bf16x8(
@@ -397,7 +413,7 @@ __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          kf, qf[qb][ks], (ks == 0 && (MAX_ONLY || ZERO)) ? f32x16{} : s[qb], 0, 0, 0);
+          kf, qf[qb][ks], ks == 0 ? f32x16{} : s[qb], 0, 0, 0);
   }
 
   if (masked) {  // uniform: tail tiles and the last partial prefix tile
@@ -416,7 +432,7 @@ __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
       float m = s[qb][0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) m = fmaxf(m, s[qb][v]);
-      rs[qb].m = fmaxf(rs[qb].m, pair_max(m));
+      rs[qb].m = fmaxf(rs[qb].m, c * pair_max(m));  // c > 0
     }
     return;
   }
@@ -424,7 +440,7 @@ __device__ inline void compute_subtile(const char *kt, const char *vt, int key0,
   // recomputation), and a row sum out of range is caught at the end of the unit.
   bf16x8 pb[kQB][2];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[qb], 0.0f, pb[qb], rs[qb].l);
+  for (int qb = 0; qb < kQB; ++qb) probs_to_bf16<ZERO>(s[qb], c, rs[qb].m, pb[qb], rs[qb].l);
   pv_product<D>(vt, key0, pb, o);
 }
 
@@ -441,7 +457,7 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
                                          bf16x8 (&qf)[kQB][D / 16], f32x16 (&o)[kQB][D / 32],
                                          RowState (&rs)[kQB], const TileRsrc &load_src,
                                          char *next_k, char *next_v, int wave,
-                                         const LoadPlan<D> &plan) {
+                                         const LoadPlan<D> &plan, float c) {
   constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
   constexpr int kSteps = 2 * (D / 16);  // score MFMA steps (each kQB MFMAs) in the tile
   // Raised wave priority for the score MFMAs: the SIMD issues this wave's matrix burst ahead
@@ -478,7 +494,8 @@ __device__ inline void compute_tile_fast(const char *kt, const char *vt,
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) probs_to_bf16(s[sub][qb], 0.0f, pb[sub][qb], rs[qb].l);
+    for (int qb = 0; qb < kQB; ++qb)
+      probs_to_bf16<true>(s[sub][qb], c, 0.0f, pb[sub][qb], rs[qb].l);
     pv_product<D>(vt, 32 * sub, pb[sub], o);
   }
 }
@@ -487,6 +504,8 @@ struct Unit {
   int qa, qz, posz;  // questions touched by the workgroup; last row's position in qz
   int plen;          // the unit's prefix: rows [pstart, pstart + plen) of the prefix K/V
   int64_t pstart;
+  int kbeg, kend;    // the prefix keys the unit walks: [kbeg, kend) (0, plen unless split)
+  bool tail;         // the unit walks its questions' tail keys (all but non-last pieces)
 };
 
 __device__ inline TileSrc tail_from(const Args &a, const Tables &tab, const Unit &u, int q) {
@@ -509,13 +528,18 @@ __device__ inline TileSrc tail_from(const Args &a, const Tables &tab, const Unit
 }
 
 __device__ inline TileSrc first_tile(const Args &a, const Tables &tab, const Unit &u) {
-  if (u.plen > 0) {
+  if (u.kbeg < u.kend) {
     TileSrc s{};
     s.rowbase = u.pstart;
-    s.kstart = 0;
-    s.klimit = u.plen;
+    s.kstart = u.kbeg;
+    s.klimit = u.kend;
     s.q = -1;
     s.valid = true;
+    return s;
+  }
+  if (!u.tail) {
+    TileSrc s{};
+    s.valid = false;
     return s;
   }
   return tail_from(a, tab, u, u.qa);
@@ -526,6 +550,10 @@ __device__ inline TileSrc next_tile(const Args &a, const Tables &tab, const Unit
   if (!s.valid) return s;
   s.kstart += kTileKeys;
   if (s.kstart < s.klimit) return s;
+  if (s.q < 0 && !u.tail) {
+    s.valid = false;
+    return s;
+  }
   return tail_from(a, tab, u, s.q < 0 ? u.qa : s.q + 1);
 }
 
@@ -604,7 +632,7 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
     const bool fast = !max_only && zero_ref && whole;
     if (active && fast) {
       compute_tile_fast<D>(sm.k[stage] + klane, sm.v[stage] + vlane, qf, o, rs, ra,
-                           sm.k[stage2], sm.v[stage2], wave, plan);
+                           sm.k[stage2], sm.v[stage2], wave, plan, a.scale_log2);
     } else {
 #pragma unroll
       for (int i = 0; i < Layout<D>::FULL; ++i)
@@ -623,18 +651,19 @@ __device__ inline void run_tiles(const Args &a, Smem<D> &sm, const Unit &u, int 
         for (int qb = 0; qb < kQB; ++qb) {
           int last;  // last visible key of this row, relative to the sub-tile start
           if (cur.q < 0)
-            last = cur.klimit - 1 - base;  // a prefix tile's klimit is the prefix length
+            last = cur.klimit - 1 - base;  // a prefix tile's klimit ends the unit's prefix keys
           else
             last = (rt.rq[qb] == cur.q) ? rt.rpos[qb] - base : -1;
           last = min(last, 31);
           lim[qb] = last - 4 * half;
         }
         if (max_only)
-          compute_subtile<D, true, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+          compute_subtile<D, true, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim, a.scale_log2);
         else if (zero_ref)
-          compute_subtile<D, false, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+          compute_subtile<D, false, true>(kt, vt, 32 * sub, qf, o, rs, masked, lim, a.scale_log2);
         else
-          compute_subtile<D, false, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim);
+          compute_subtile<D, false, false>(kt, vt, 32 * sub, qf, o, rs, masked, lim,
+                                           a.scale_log2);
       }
     }
 
@@ -738,6 +767,50 @@ __device__ inline void store_rows(const Args &a, char *stage, const f32x16 (&o)[
   }
 }
 
+// Floats one lane of a key-split piece leaves for the merge: its D/2 sums of O (the accumulator
+// registers, in their MFMA layout), its row's reference m and its part l of the row sum.
+__host__ __device__ constexpr int part_floats(int d) { return d / 2 + 2; }
+
+// This wave's partial sums of a piece, register by register, lanes contiguous (each register is
+// one 256-byte store of the wave): slot (piece, KV head g, wave) of `part`.
+template <int D>
+__device__ inline void write_partials(const Args &a, int64_t piece, int g, int wave, int lane,
+                                      const f32x16 (&o)[kQB][D / 32], const RowState (&rs)[kQB]) {
+  float *base =
+      a.part + ((piece * a.hkv + g) * kWaves + wave) * int64_t(part_floats(D)) * 64 + lane;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) base[(db * 16 + v) * 64] = o[0][db][v];
+  base[(D / 2) * 64] = rs[0].m;
+  base[(D / 2 + 1) * 64] = rs[0].l;
+}
+
+// The merge pass for this wave's rows of base unit `bu`: the pieces' sums, each scaled by
+// 2^(m_j - M) for the largest reference M (all 0 unless a piece recomputed exactly), added in
+// piece order into o and rs (rs.l stays this lane's part of the row sum).
+template <int D>
+__device__ inline void merge_partials(const Args &a, int64_t bu, int g, int wave, int lane,
+                                      f32x16 (&o)[kQB][D / 32], RowState (&rs)[kQB]) {
+  const int ways = a.split_ways;
+  const int64_t stride = int64_t(part_floats(D)) * 64;
+  auto slot = [&](int j) {
+    return a.part + (((bu * ways + j) * a.hkv + g) * kWaves + wave) * stride + lane;
+  };
+  float m = -INFINITY;
+  for (int j = 0; j < ways; ++j) m = fmaxf(m, slot(j)[(D / 2) * 64]);
+  init_rows<D>(o, rs, m);
+  for (int j = 0; j < ways; ++j) {
+    const float *p = slot(j);
+    const float f = __builtin_amdgcn_exp2f(p[(D / 2) * 64] - m);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[0][db][v] += f * p[(db * 16 + v) * 64];
+    rs[0].l += f * p[(D / 2 + 1) * 64];
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -760,10 +833,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const int64_t R = valid_total * G;
   Unit u;
   int64_t row0, row_end;
-  if (a.n_req == 1) {
-    row0 = unit < a.full_units ? unit * kRowsPerUnit
-                               : a.full_units * kRowsPerUnit + (unit - a.full_units) * a.small_rows;
-    row_end = row0 + (unit < a.full_units ? int64_t(kRowsPerUnit) : int64_t(a.small_rows));
+  int64_t piece = -1;  // this workgroup's key-split piece, if it is one
+  u.kbeg = 0;
+  u.tail = true;
+  if (a.merge) {  // `unit` is a split base unit; its pieces have run
+    row0 = a.split_row0 + unit * kRowsPerUnit;
+    row_end = row0 + kRowsPerUnit;
+    u.plen = a.req_plen[0];
+    u.pstart = a.req_pstart[0];
+  } else if (a.n_req == 1) {
+    if (unit >= a.split_first) {
+      piece = unit - a.split_first;
+      const int64_t bu = piece / a.split_ways;
+      const int j = int(piece % a.split_ways);
+      row0 = a.split_row0 + bu * kRowsPerUnit;
+      row_end = row0 + kRowsPerUnit;
+      u.kbeg = min(j * a.split_tiles * kTileKeys, a.req_plen[0]);
+      u.tail = j == a.split_ways - 1;
+    } else {
+      row0 = unit < a.full_units
+                 ? unit * kRowsPerUnit
+                 : a.full_units * kRowsPerUnit + (unit - a.full_units) * a.small_rows;
+      row_end = row0 + (unit < a.full_units ? int64_t(kRowsPerUnit) : int64_t(a.small_rows));
+    }
     u.plen = a.req_plen[0];
     u.pstart = a.req_pstart[0];
   } else {
@@ -777,6 +869,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     u.plen = a.req_plen[r];
     u.pstart = a.req_pstart[r];
   }
+  u.kend = u.plen;
+  if (piece >= 0)
+    u.kend = min((int(piece % a.split_ways) + 1) * a.split_tiles * kTileKeys, u.plen);
   row_end = min(R, row_end);
   if (row0 < 0 || row0 >= row_end) return;  // uniform across the workgroup
 
@@ -801,11 +896,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   // The ring's first pair of K/V tiles goes out before the query rows are fetched, so the
   // two latencies overlap.
   const TileSrc first = first_tile(a, sm.tab, u);
-  if (!first.valid) return;  // uniform: nothing visible (cannot happen for a valid table)
+  if (!first.valid && !a.merge) return;  // uniform: nothing visible (not for a valid table)
   const LoadPlan<D> plan = make_load_plan<D>(a, wave, lane);
-  start_tiles<D>(a, sm, u, g, first, wave, plan);
+  if (!a.merge) start_tiles<D>(a, sm, u, g, first, wave, plan);
 
-  // This lane's query rows: Q pre-scaled by scale * log2(e), rounded to bf16 once.
+  // This lane's query rows, as given (the scale is applied to the FP32 scores).
   bool rvalid[kQB];
   int rq[kQB], rpos[kQB], rhead[kQB];
   int64_t rtok[kQB];
@@ -830,12 +925,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (rvalid[qb]) v = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
-      const bf16x8 x = as_bf16x8(v);
-      bf16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * a.scale_log2);
-      qf[qb][ks] = y;
+      if (rvalid[qb] && !a.merge) v = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
+      qf[qb][ks] = as_bf16x8(v);
     }
   }
 
@@ -849,6 +940,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
   const WaveSpan ws{wave_active, wqa, wqz, wposz, wposa};
   f32x16 o[kQB][D / 32];
   RowState rs[kQB];
+  if (a.merge) {
+    merge_partials<D>(a, unit, g, wave, lane, o, rs);
+    store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
+    return;
+  }
   init_rows<D>(o, rs, 0.0f);
   run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
                true, true);
@@ -860,7 +956,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     const float l = pair_sum(rs[qb].l);
     over |= rvalid[qb] && !(l <= kSumLimit && l >= kSumFloor);
   }
-  store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
+  if (piece >= 0)
+    write_partials<D>(a, piece, g, wave, lane, o, rs);
+  else
+    store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
   // Did any wave of the workgroup overflow? (The flag was cleared before the first barrier.)
   // The barrier orders only the flag in LDS, so the workgroup does not wait for its stores to
   // complete: it ends, and the next one starts on this CU, while they drain.
@@ -876,7 +975,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_tail_attention_kernel(Args
     init_rows<D>(o, rs, __builtin_nanf(""));
     run_tiles<D>(a, sm, u, g, first, rt, ws, klane, vlane, wave, lane, plan, qf, o, rs, false,
                  false, false);
-    store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
+    if (piece >= 0)
+      write_partials<D>(a, piece, g, wave, lane, o, rs);
+    else
+      store_rows<D>(a, ostage, o, rs, rvalid, rtok, rhead, lane);
   }
 #endif
 }
@@ -912,6 +1014,44 @@ inline int64_t unit_split(int64_t rows, int hkv, int cus, int64_t &full_units, i
   full_units = full;
   small_rows = int(small_up);
   return full + (rem + small_up - 1) / small_up;
+}
+
+// Key split of the last round (a single request with a prefix, given workspace for the pieces'
+// sums). When a head's rows need more than one round of 384-row units and the units left after
+// the full rounds would leave CUs idle, each of those R units is cut by prefix keys into
+// ways = cus / hkv / R pieces (each a run of whole 64-key tiles, the tail keys with the last
+// piece), so the last round is R * ways pieces of full 384-row units, about one per CU, each a
+// ways-th of a unit's keys, instead of smaller row units with fewer waves per SIMD; a merge pass
+// then adds each unit's pieces. Fills the plan and returns true, or returns false (no split).
+struct SplitPlan {
+  int64_t full;   // 384-row units per head before the split ones
+  int64_t split;  // split base units per head (R)
+  int ways;       // pieces per split unit
+  int tiles;      // prefix tiles per piece
+};
+
+inline bool split_plan(int64_t rows, int hkv, int cus, int prefix_len, SplitPlan &sp) {
+  const int64_t units = (rows + kRowsPerUnit - 1) / kRowsPerUnit;
+  const int64_t per_round = cus / hkv;
+  if (per_round < 2 || units <= per_round) return false;
+  const int64_t full = units / per_round * per_round;
+  const int64_t left = units - full;
+  if (left == 0) return false;
+  const int64_t ways = per_round / left;
+  const int64_t prefix_tiles = (prefix_len + kTileKeys - 1) / kTileKeys;
+  if (ways < 2 || prefix_tiles < 2 * ways) return false;
+  sp.full = full;
+  sp.split = left;
+  sp.tiles = int((prefix_tiles + ways - 1) / ways);
+  // Recount the pieces for that piece size, so that none of them is left without a tile
+  // (a piece with no keys would write no partial results); at least 2 remain.
+  sp.ways = int((prefix_tiles + sp.tiles - 1) / sp.tiles);
+  return true;
+}
+
+inline size_t split_workspace_bytes(const SplitPlan &sp, int hkv, int head_dim) {
+  return size_t(sp.split) * size_t(sp.ways) * size_t(hkv) * size_t(kWaves) * 64 *
+         size_t(part_floats(head_dim)) * sizeof(float);
 }
 
 // Work split of a grouped launch, with `rows[r]` query rows per KV head in request r: the
@@ -960,6 +1100,13 @@ hipError_t launch(const Args &a, hipStream_t stream) {
   const int64_t blocks = a.n_units * a.hkv;  // exactly n_units units per KV head
   hipLaunchKernelGGL(prefix_tail_attention_kernel<D>, dim3(unsigned(blocks)), dim3(kThreads), 0,
                      stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.split_first >= a.n_units) return err;
+  Args m = a;  // the merge pass: one workgroup per split base unit and KV head
+  m.merge = 1;
+  m.n_units = (a.n_units - a.split_first) / a.split_ways;
+  hipLaunchKernelGGL(prefix_tail_attention_kernel<D>, dim3(unsigned(m.n_units * a.hkv)),
+                     dim3(kThreads), 0, stream, m);
   return hipGetLastError();
 }
 
@@ -1045,7 +1192,34 @@ int device_cus(int &cus) {
   return BLINK_OK;
 }
 
+// The key-split plan of a single-request launch on the current device, if any; `cus` is set.
+int single_plan(int64_t total_valid_tokens, int32_t n_heads_q, int32_t n_heads_kv,
+                int32_t prefix_len, int &cus, SplitPlan &sp, bool &split) {
+  int rc = device_cus(cus);
+  if (rc != BLINK_OK) return rc;
+  split = split_plan(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv, cus, prefix_len,
+                     sp);
+  return BLINK_OK;
+}
+
 }  // namespace
+
+extern "C" size_t blink_prefix_tail_attention_workspace(int64_t total_valid_tokens,
+                                                        int32_t n_heads_q, int32_t n_heads_kv,
+                                                        int32_t head_dim, int32_t prefix_len) {
+  if (total_valid_tokens < 1 || n_heads_kv < 1 || n_heads_q < n_heads_kv ||
+      n_heads_q % n_heads_kv || (head_dim != 64 && head_dim != 128) || prefix_len < 0 ||
+      total_valid_tokens > int64_t(BLINK_MAX_QUESTIONS) * BLINK_MAX_INPUT_TOKENS)
+    return 0;
+  int cus = 0;
+  SplitPlan sp{};
+  bool split = false;
+  if (single_plan(total_valid_tokens, n_heads_q, n_heads_kv, prefix_len, cus, sp, split) !=
+          BLINK_OK ||
+      !split)
+    return 0;
+  return split_workspace_bytes(sp, n_heads_kv, head_dim);
+}
 
 extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, const void *v_tail,
                                            const void *k_prefix, const void *v_prefix, void *out,
@@ -1054,7 +1228,8 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
                                            int64_t total_valid_tokens,
                                            int64_t total_padded_tokens, int32_t prefix_len,
                                            int32_t n_heads_q, int32_t n_heads_kv,
-                                           int32_t head_dim, float scale, void *stream) {
+                                           int32_t head_dim, float scale, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
   using blink::fail;
   const Shape sh{n_questions, total_valid_tokens, total_padded_tokens, n_heads_q, n_heads_kv,
                  head_dim, scale};
@@ -1065,11 +1240,29 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
                 "context length is %d", prefix_len, BLINK_MAX_INPUT_TOKENS);
   if (prefix_len > 0 && (!k_prefix || !v_prefix))
     return fail(BLINK_E_INVALID, "prefix K/V pointers are NULL with prefix_len %d", prefix_len);
+  if (workspace && !blink::aligned16(workspace))
+    return fail(BLINK_E_INVALID, "the workspace must be 16-byte aligned");
   int cus = 0;
-  if ((rc = device_cus(cus)) != BLINK_OK) return rc;
+  SplitPlan sp{};
+  bool split = false;
+  if ((rc = single_plan(total_valid_tokens, n_heads_q, n_heads_kv, prefix_len, cus, sp, split)) !=
+      BLINK_OK)
+    return rc;
   Args a{};
-  a.n_units = unit_split(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv, cus,
-                         a.full_units, a.small_rows);
+  if (split && workspace && workspace_bytes >= split_workspace_bytes(sp, n_heads_kv, head_dim)) {
+    a.full_units = sp.full;
+    a.small_rows = kRowsPerUnit;
+    a.split_first = sp.full;
+    a.split_ways = sp.ways;
+    a.split_tiles = sp.tiles;
+    a.split_row0 = sp.full * kRowsPerUnit;
+    a.part = static_cast<float *>(workspace);
+    a.n_units = sp.full + sp.split * sp.ways;
+  } else {
+    a.n_units = unit_split(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv, cus,
+                           a.full_units, a.small_rows);
+    a.split_first = a.n_units;
+  }
   a.prefix_rows = prefix_len;
   a.n_req = 1;
   a.req_first[0] = 0;
@@ -1148,6 +1341,7 @@ extern "C" int blink_prefix_tail_attention_grouped(
   a.req_unit[n_requests] = units;
   a.n_units = units;
   a.full_units = units;
+  a.split_first = units;  // no key split in a grouped launch
   return run(a, q, k_tail, v_tail, k_prefix, v_prefix, out, d_token_offset, d_valid_start, sh,
              stream);
 }

@@ -63,8 +63,9 @@ def bf16_to_f32_host(t):
     return synth.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
 
 
-def run_attention(req, tensors=None, token_offset=None, tail_len=None):
-    """GPU attention through the C ABI; returns the output as float32 numpy [T_pad, H_q, D]."""
+def run_attention(req, tensors=None, token_offset=None, tail_len=None, workspace="auto"):
+    """GPU attention through the C ABI; returns the output as float32 numpy [T_pad, H_q, D].
+    ``workspace``: "auto" (what the library asks for: the bench's launch) or None (none)."""
     import torch
 
     import pass_typed_decision_amd as blink
@@ -83,7 +84,8 @@ def run_attention(req, tensors=None, token_offset=None, tail_len=None):
     np.cumsum(tail, out=vs[1:])
     d_off = torch.as_tensor(np.asarray(offs, np.int64)).cuda()
     d_vs = torch.as_tensor(vs).cuda()
-    blink.prefix_tail_attention(q, kt, vt, kp, vp, out, d_off, d_vs, int(vs[-1]), cfg.scale)
+    blink.prefix_tail_attention(q, kt, vt, kp, vp, out, d_off, d_vs, int(vs[-1]), cfg.scale,
+                                workspace=workspace)
     torch.cuda.synchronize()
     return bf16_to_f32_host(out)
 
@@ -172,8 +174,33 @@ ROWS_PER_UNIT = 384
 SIMD_ROWS = 128
 
 
-def attention_units(rows, hkv, cus):
-    """[(row0, row_end)] of every unit of one KV head, in unit order."""
+def attention_split(rows, hkv, cus, prefix_len):
+    """The launcher's key split of the last round, given a workspace: (full units, split base
+    units, pieces per unit, prefix tiles per piece), or None. When a head's 384-row units need
+    more than one round and the units left after the full rounds would leave CUs idle, each of
+    them runs as several pieces over disjoint runs of 64-key prefix tiles."""
+    units = -(-rows // ROWS_PER_UNIT)
+    per_round = cus // hkv
+    if per_round < 2 or units <= per_round:
+        return None
+    full = units // per_round * per_round
+    left = units - full
+    if left == 0:
+        return None
+    ways = per_round // left
+    tiles = -(-prefix_len // 64)
+    if ways < 2 or tiles < 2 * ways:
+        return None
+    per = -(-tiles // ways)
+    return full, left, -(-tiles // per), per
+
+
+def attention_units(rows, hkv, cus, prefix_len=0, split=False):
+    """[(row0, row_end)] of every unit of one KV head, in unit order (with `split`: as launched
+    with a workspace, where a key split keeps whole 384-row units)."""
+    if split and attention_split(rows, hkv, cus, prefix_len):
+        n = -(-rows // ROWS_PER_UNIT)
+        return [(i * ROWS_PER_UNIT, min(rows, (i + 1) * ROWS_PER_UNIT)) for i in range(n)]
     units = -(-rows // ROWS_PER_UNIT)
     full, small = units, ROWS_PER_UNIT
     per_round = cus // hkv
@@ -200,9 +227,10 @@ def attention_units(rows, hkv, cus):
     return out
 
 
-def unit_samples(req, cus):
+def unit_samples(req, cus, split=True):
     """(question, position, head) at the first and last row of every (unit, KV head) of the
-    attention launch, plus the first and last token of every tail."""
+    attention launch (with `split`: launched with a workspace), plus the first and last token
+    of every tail."""
     cfg = req.cfg
     g_size = cfg.n_heads_q // cfg.n_heads_kv
     vs = req.valid_start()
@@ -210,7 +238,8 @@ def unit_samples(req, cus):
     for i, n in enumerate(req.tail_len):
         for t in {0, int(n) - 1}:
             picks.add((i, t, (i * 7 + t) % cfg.n_heads_q))
-    for row0, row_end in attention_units(int(vs[-1]) * g_size, cfg.n_heads_kv, cus):
+    for row0, row_end in attention_units(int(vs[-1]) * g_size, cfg.n_heads_kv, cus,
+                                         cfg.prefix_len, split):
         for r in {row0, row_end - 1}:
             c, hl = divmod(r, g_size)
             q = int(np.searchsorted(vs, c, side="right") - 1)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(blink):
     lib = ctypes.CDLL(blink.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert blink.load_library().blink_abi_version() == 8
+    assert blink.load_library().blink_abi_version() == 9
 
 
 def _compare(pk, ref):
@@ -156,11 +156,12 @@ def test_readout_refusals_before_launch(blink, kw, code, msg):
 
 
 def _attention(lib, n=2, total=10, t_pad=12, prefix=0, hq=4, hkv=1, d=64, scale=0.125,
-               null_prefix=True):
+               null_prefix=True, workspace=None):
     fake = ctypes.c_void_p(256)
     pre = None if null_prefix else fake
     return lib.blink_prefix_tail_attention(fake, fake, fake, pre, pre, fake, fake, fake, n,
-                                           total, t_pad, prefix, hq, hkv, d, scale, None)
+                                           total, t_pad, prefix, hq, hkv, d, scale, workspace,
+                                           1 << 20 if workspace else 0, None)
 
 
 @pytest.mark.parametrize("kw, code, msg", [
@@ -173,11 +174,20 @@ def _attention(lib, n=2, total=10, t_pad=12, prefix=0, hq=4, hkv=1, d=64, scale=
     (dict(prefix=131072, null_prefix=False), -2, "maximum context length is 131072"),
     (dict(total=20, t_pad=12), -1, "token totals do not fit"),
     (dict(total=1), -1, "token totals do not fit"),
+    (dict(workspace=ctypes.c_void_p(264)), -1, "workspace must be 16-byte aligned"),
 ])
 def test_attention_refusals_before_launch(blink, kw, code, msg):
     lib = blink.load_library()
     assert _attention(lib, **kw) == code
     assert msg in lib.blink_last_error().decode()
+
+
+def test_attention_workspace_query_refuses_bad_sizes(blink):
+    # Sizes the launch would refuse ask for no workspace (without a device every size gets 0).
+    lib = blink.load_library()
+    for args in [(0, 32, 8, 128, 2048), (5000, 6, 4, 128, 0), (5000, 32, 8, 96, 2048),
+                 (5000, 32, 8, 128, -1), (512 * 131072 + 1, 32, 8, 128, 0)]:
+        assert lib.blink_prefix_tail_attention_workspace(*args) == 0
 
 
 def test_error_text_is_cleared_by_success(blink):

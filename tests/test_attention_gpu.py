@@ -2,7 +2,8 @@
 
 Bar: max-abs 2e-2 on the bf16 outputs of every real row. Reduced variants of all five
 workloads run whole against the oracle (several tiles, ragged tails, GQA 4 and 5, with and
-without a prefix); the full-size workloads are launched exactly as the bench launches them and
+without a prefix), and reduced requests that take the key split of the last round; the full-size
+workloads are launched exactly as the bench launches them and
 checked whole (4B-like, plain max packing) or at the first and last row of every unit of work
 of the launch (long document, 27B-like). Invariants (padding content, batch composition, head permutation)
 must hold bit for bit."""
@@ -11,7 +12,8 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import ATTN_TOL, Request, run_attention, sample_rows, unit_samples, valid_rows
+from helpers import (ATTN_TOL, Request, attention_split, run_attention, sample_rows, unit_samples,
+                     valid_rows)
 from oracle.attention import attention_full, attention_rows
 
 pytestmark = pytest.mark.gpu
@@ -106,6 +108,46 @@ def test_full_size_every_unit(number):
     assert np.isfinite(got[valid_rows(req)]).all()
 
 
+# Launches that take the key split of the last round (with a workspace): the 384-row units left
+# after the full rounds run as 2, 4 or 5 pieces over runs of prefix tiles (ragged last tile, the
+# tail in the last piece only), and a merge pass joins their partial results. Sized so that each
+# lands in the split at 256 CUs; whole output against the oracle, and within the bar of the
+# unsplit launch of the same request.
+SPLIT = {
+    "ways2_d128": synth.config(5, prefix_len=1000, n_questions=12, tail_lo=250, tail_hi=330),
+    "ways4_d128": synth.config(5, prefix_len=900, n_questions=10, tail_lo=280, tail_hi=320),
+    "ways5_d128": synth.config(5, prefix_len=1500, n_questions=10, tail_lo=265, tail_hi=300),
+    "ways4_d64_group4": synth.config(1, n_heads_q=16, n_heads_kv=4, prefix_len=700,
+                                     n_questions=200, tail_lo=30, tail_hi=45),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT))
+def test_key_split_matches_oracle_whole(name):
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = SPLIT[name]
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tokens = int(np.sum(req.tail_len))
+    group = cfg.n_heads_q // cfg.n_heads_kv
+    plan = attention_split(tokens * group, cfg.n_heads_kv, cus, cfg.prefix_len)
+    print(f"attention key split: {name} ({tokens} tokens, {cus} CUs) plan {plan}", flush=True)
+    assert plan is not None, "the request no longer lands in the key split"
+    assert blink.attention_workspace(tokens, cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim,
+                                     cfg.prefix_len) is not None
+    got = run_attention(req)
+    ref = _oracle(req)
+    err = _max_err_by_question(req, got, ref)
+    plain = run_attention(req, workspace=None)
+    rows = valid_rows(req)
+    gap = float(np.abs(got[rows] - plain[rows]).max())
+    print(f"  max abs err {err:.3e}; split vs unsplit {gap:.3e}", flush=True)
+    assert err <= ATTN_TOL and gap <= ATTN_TOL
+
+
 # The largest context the boundary accepts (prefix + tail = 131072 tokens): one question whose
 # tail is the whole context with no prefix (2048 tiles of causal tail attention, as when the
 # prefix itself is encoded), and the longest prefix with a one-token tail.
@@ -152,15 +194,18 @@ def test_padding_content_is_never_read():
 
 
 def test_question_alone_is_bitwise_identical():
+    # Launches without a workspace: a row's result does not depend on the rest of the batch.
+    # (With one, rows in key-split units are summed in another order: equal up to rounding.)
     cfg = SMALL["4b_like_small"]
     req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
-    packed = run_attention(req)
+    packed = run_attention(req, workspace=None)
     for i in range(len(req.tail_len)):
         off, n = req.pack["token_offset"][i], int(req.tail_len[i])
         alone_ts = dict(req.tensors)
         for name in ("q", "k_tail", "v_tail"):
             alone_ts[name] = np.ascontiguousarray(req.tensors[name][off:off + n])
-        alone = run_attention(req, tensors=alone_ts, token_offset=[0], tail_len=[n])
+        alone = run_attention(req, tensors=alone_ts, token_offset=[0], tail_len=[n],
+                              workspace=None)
         np.testing.assert_array_equal(alone, packed[off:off + n])
 
 
@@ -212,6 +257,10 @@ EXTREMES = {
     "plain_tail_past_headroom": (synth.config(4, n_questions=12, tail_lo=100, tail_hi=200),
                                  "tail", 130, 6.0),
     "d64_prefix_past_headroom": (SMALL["d64_group1"], "prefix", 100, 8.0),
+    # key split: only the first piece's rows recompute, so the merge joins pieces with
+    # different references
+    "split_first_piece_past_headroom": (SPLIT["ways4_d128"], "prefix", 100, 6.0),
+    "split_last_piece_past_headroom": (SPLIT["ways2_d128"], "prefix", 990, 6.0),
 }
 
 

@@ -1,7 +1,8 @@
 """The attention launch's work split, checked on the host: builds tests/unit_plan_check.hip
-with hipcc (host code only runs) and runs it over random request layouts; then checks that the
-tests' restatement of the split (helpers.attention_units, which places the per-unit parity
-samples) matches the launcher's own planner."""
+with hipcc (host code only runs) and runs it over random request layouts (row re-cut, grouped
+split, key split of the last round); then checks that the tests' restatement of the split
+(helpers.attention_units and attention_split, which place the per-unit parity samples) matches
+the launcher's own planners."""
 import os
 import shutil
 import subprocess
@@ -9,7 +10,7 @@ import subprocess
 import numpy as np
 import pytest
 
-from helpers import attention_units
+from helpers import attention_split, attention_units
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -45,25 +46,32 @@ def test_unit_planners_cover_every_row_once(checker):
     assert run.returncode == 0, run.stdout + run.stderr
     assert "two requests: 120 units, full 56 40, small 384 256" in run.stdout
     assert "ok: 100000 layouts each" in run.stdout
+    assert "27B-like split: full 128, split 14, ways 2, tiles 512" in run.stdout
 
 
 def test_sample_plan_matches_launcher(checker):
     rng = np.random.default_rng(7)
     # The five workloads' rows per KV head (seeded tails; 4B-like 5338 x 4, long document
     # 21113 x 4, plain max packing 74300 x 4, 27B-like 10443 x 5), then random sizes.
-    cases = [(5338 * 4, 8, 256), (21113 * 4, 8, 256), (74300 * 4, 8, 256), (10443 * 5, 8, 256),
-             (139 * 4, 1, 256)]
+    cases = [(5338 * 4, 8, 256, 2048), (21113 * 4, 8, 256, 18432), (74300 * 4, 8, 256, 0),
+             (10443 * 5, 8, 256, 65536), (139 * 4, 1, 256, 256)]
     for _ in range(3000):
         cases.append((int(rng.integers(1, [64, 2000, 30000, 400000][rng.integers(4)])),
                       int(1 << rng.integers(4)), int(256 if rng.integers(3) == 0 else
-                                                     rng.integers(1, 300))))
-    stdin = "".join(f"{r} {h} {c}\n" for r, h, c in cases)
+                                                     rng.integers(1, 300)),
+                      int(rng.integers(0, 70000))))
+    stdin = "".join(f"{r} {h} {c} {p}\n" for r, h, c, p in cases)
     run = subprocess.run([checker, "plan"], input=stdin, capture_output=True, text=True,
                          timeout=300)
     assert run.returncode == 0, run.stderr
     lines = run.stdout.split("\n")
-    for (rows, hkv, cus), line in zip(cases, lines):
-        units, full, small = (int(x) for x in line.split())
+    for (rows, hkv, cus, prefix), line in zip(cases, lines):
+        units, full, small, s_full, s_left, ways, tiles = (int(x) for x in line.split())
+        split = attention_split(rows, hkv, cus, prefix)
+        assert split == ((s_full, s_left, ways, tiles) if ways else None), (rows, hkv, cus, prefix)
+        if split:  # the key split keeps whole 384-row units
+            assert attention_units(rows, hkv, cus, prefix, True) == [
+                (i * 384, min(rows, (i + 1) * 384)) for i in range(s_full + s_left)]
         plan = attention_units(rows, hkv, cus)
         assert len(plan) == units, (rows, hkv, cus)
         sizes = [b - a for a, b in plan]

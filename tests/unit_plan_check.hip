@@ -36,6 +36,25 @@ bool check_single(int64_t rows, int hkv, int cus) {
   return rounds_of(units, cus / hkv) == rounds_of(whole, cus / hkv);
 }
 
+// The key split: full units then the split base units cover every row once; each base unit's
+// pieces (key ranges computed as the kernel does) cover the prefix keys once, in order, each
+// piece non-empty, only the last one walking the tail; the pieces fill at most one round.
+bool check_split(int64_t rows, int hkv, int cus, int prefix) {
+  SplitPlan sp{};
+  if (!split_plan(rows, hkv, cus, prefix, sp)) return true;
+  const int64_t units = (rows + kRowsPerUnit - 1) / kRowsPerUnit;
+  if (sp.full + sp.split != units || sp.full % (cus / hkv) != 0) return false;
+  if (sp.split * sp.ways > cus / hkv || sp.ways < 2 || sp.tiles < 1) return false;
+  int covered = 0;
+  for (int j = 0; j < sp.ways; ++j) {
+    const int kbeg = std::min(j * sp.tiles * kTileKeys, prefix);
+    const int kend = std::min((j + 1) * sp.tiles * kTileKeys, prefix);
+    if (kbeg != covered || kbeg >= kend) return false;
+    covered = kend;
+  }
+  return covered == prefix;
+}
+
 bool check_grouped(const std::vector<int64_t> &rows, int hkv, int cus) {
   const int n_req = int(rows.size());
   int full[kMaxRequests], small[kMaxRequests];
@@ -75,19 +94,23 @@ bool check_grouped(const std::vector<int64_t> &rows, int hkv, int cus) {
 }  // namespace
 
 int main(int argc, char **argv) {
-  if (argc > 1) {  // "plan": one "rows hkv cus" per input line -> "units full_units small_rows"
+  if (argc > 1) {  // "plan": "rows hkv cus prefix" per line -> "units full small" of the row
+                   // split, then "full left ways tiles" of the key split (zeros if none)
     long long rows = 0;
-    int hkv = 0, cus = 0;
-    while (scanf("%lld %d %d", &rows, &hkv, &cus) == 3) {
+    int hkv = 0, cus = 0, prefix = 0;
+    while (scanf("%lld %d %d %d", &rows, &hkv, &cus, &prefix) == 4) {
       int64_t full = 0;
       int small = 0;
       const int64_t units = unit_split(rows, hkv, cus, full, small);
-      printf("%lld %lld %d\n", (long long)units, (long long)full, small);
+      SplitPlan sp{};
+      if (!split_plan(rows, hkv, cus, prefix, sp)) sp = SplitPlan{0, 0, 0, 0};
+      printf("%lld %lld %d %lld %lld %d %d\n", (long long)units, (long long)full, small,
+             (long long)sp.full, (long long)sp.split, sp.ways, sp.tiles);
     }
     return 0;
   }
   std::mt19937_64 rng(20261202);
-  long recut_single = 0, recut_grouped = 0;
+  long recut_single = 0, recut_grouped = 0, split_single = 0;
   for (int trial = 0; trial < 100000; ++trial) {
     const int hkv = 1 << (rng() % 4);
     const int cus = trial % 3 == 0 ? 256 : int(1 + rng() % 300);
@@ -97,6 +120,14 @@ int main(int argc, char **argv) {
       printf("FAIL unit_split rows %lld hkv %d cus %d\n", (long long)rows, hkv, cus);
       return 1;
     }
+    const int prefix = int(rng() % 70000);
+    if (!check_split(rows, hkv, cus, prefix)) {
+      printf("FAIL split_plan rows %lld hkv %d cus %d prefix %d\n", (long long)rows, hkv, cus,
+             prefix);
+      return 1;
+    }
+    SplitPlan sp{};
+    split_single += split_plan(rows, hkv, cus, prefix, sp);
     int64_t full = 0;
     int small = 0;
     unit_split(rows, hkv, cus, full, small);
@@ -125,7 +156,13 @@ int main(int argc, char **argv) {
   const int64_t units = grouped_split(two, 2, 8, 256, fl, sm);
   printf("two requests: %lld units, full %d %d, small %d %d\n", (long long)units, fl[0], fl[1],
          sm[0], sm[1]);
-  printf("ok: 100000 layouts each, re-cut %ld single, %ld grouped\n", recut_single,
-         recut_grouped);
+  // The 27B-like request as drawn: 10864 tokens x 5 query heads per KV head, 8 KV heads, 256
+  // CUs, a 65536-token prefix.
+  SplitPlan c5{};
+  split_plan(54320, 8, 256, 65536, c5);
+  printf("27B-like split: full %lld, split %lld, ways %d, tiles %d\n", (long long)c5.full,
+         (long long)c5.split, c5.ways, c5.tiles);
+  printf("ok: 100000 layouts each, re-cut %ld single, %ld grouped, key-split %ld\n",
+         recut_single, recut_grouped, split_single);
   return 0;
 }
