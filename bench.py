@@ -37,14 +37,25 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
-# rocprofv3 readings of the attention kernel per launch, keyed by workload number, with the
-# sha256 of the kernel source they were taken on (a changed kernel reports null until it is
-# counted again): HBM bytes = FETCH_SIZE (x2, calibrated on a plain 1 GiB copy) + WRITE_SIZE
-# (x1); matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES over SQ_BUSY_CYCLES x SIMDs per CU.
+# rocprofv3 readings of the attention per call, keyed by workload number, with the sha256 of
+# the kernel source they were taken on (a changed kernel reports null until it is counted
+# again). HBM bytes = FETCH_SIZE (x2, calibrated on a plain 1 GiB copy) + WRITE_SIZE (x1),
+# summed over the call's dispatches (the 27B-like call is a main launch and a merge pass).
+# Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, for
+# the main launch: the share of the cycles the clock actually ran.
+_SHA = "298ccab48f744f83c05610ada361100156ac19a6c809f7f27f6e6363f2c47308"
 MEASURED_TRAFFIC = {
-    2: ("bbcb34d7994238bd06183ac9a50e873e7e2f8d7ad3c389627400b3fb691e9ce1", 123589018),
+    5: (_SHA, 3957665493),
+    2: (_SHA, 122489856),
+    4: (_SHA, 1536939989),
+    3: (_SHA, 1459715115),
 }
-MEASURED_MFMA_BUSY = {}
+MEASURED_MFMA_BUSY = {
+    5: (_SHA, 0.609),
+    2: (_SHA, 0.412),
+    4: (_SHA, 0.119),
+    3: (_SHA, 0.582),
+}
 ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
 
 
@@ -508,18 +519,31 @@ def time_sequential(step, steps: int, warmup: int, stream):
     return attn, read, elapsed
 
 
+def attention_dispatches(cfg, tail_len) -> int:
+    """Kernel dispatches of one attention call: two when the launch takes the key split of the
+    last round (main launch and merge pass), else one."""
+    import pass_typed_decision_amd as blink
+
+    ws = blink.attention_workspace(int(np.sum(tail_len)), cfg.n_heads_q, cfg.n_heads_kv,
+                                   cfg.head_dim, cfg.prefix_len)
+    return 1 if ws is None else 2
+
+
 def attention_roofline(cfg, tail_len, attn_ms: float) -> dict:
+    """The attention call against its roofline: algorithmic FLOPs (or bytes, for the plain path)
+    over the event time of the whole call (all its dispatches)."""
     flops = attention_flops(cfg, tail_len)
     abytes = attention_bytes(cfg, tail_len)
+    common = {"kernel": "prefix_tail_attention_kernel",
+              "dispatches_per_call": attention_dispatches(cfg, tail_len)}
     if cfg.prefix_len > 0:
         achieved = flops / (attn_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "kernel": "prefix_tail_attention_kernel", "work_per_launch": f"{flops:.4e} FLOP"}
+                "work_per_launch": f"{flops:.4e} FLOP", **common}
     achieved = abytes / (attn_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS, "kernel": "prefix_tail_attention_kernel",
-            "work_per_launch": f"{abytes:.4e} B"}
+            "frac": achieved / PEAK_HBM_GBPS, "work_per_launch": f"{abytes:.4e} B", **common}
 
 
 def secondary(number: int, stream, steps: int = 20, warmup: int = 5,
@@ -660,7 +684,7 @@ def main():
     n = cfg.n_questions
     roof = attention_roofline(cfg, tables.tail_len, attn_ms)
     roof["traffic"] = measured_traffic(cfg.number)
-    roof["traffic_unit"] = "HBM bytes per launch"
+    roof["traffic_unit"] = "HBM bytes per attention call (all its dispatches)"
     roof["mfma_busy_counted"] = measured_mfma_busy(cfg.number)
     roof["launch_ms"] = attn_ms
 
