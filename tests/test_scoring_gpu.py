@@ -67,17 +67,21 @@ def test_matches_oracle(d_model, vocab, n_seq, score_len):
     assert np.isfinite(got).all() and err <= TOL
 
 
-def test_full_vocabulary_sampled():
-    # 4B-like readout shapes: hidden 2560, vocab 151936; 32 sequences scored on their last 8
-    # tokens (256 rows). The oracle checks a sample of rows; the first two targets are the
-    # two ends of the vocabulary.
-    hidden, w_u, rows, targets = _case(7, 8192, 2560, 151936, 32, 8)
+@pytest.mark.parametrize("d_model, n_seq", [
+    (2560, 32),  # 4B-like width: 256 rows, the 256-row form
+    (5120, 16),  # 27B-like width: 128 rows, the 128-row form
+])
+def test_full_vocabulary_sampled(d_model, n_seq):
+    # vocab 151936; n_seq sequences scored on their last 8 tokens. The oracle checks the first
+    # and last row of every 32-row tile of the call (every row group of 64 and both of its
+    # tiles, both lane edges); the first two targets are the two ends of the vocabulary.
+    hidden, w_u, rows, targets = _case(7, 8192, d_model, 151936, n_seq, 8)
     targets[0], targets[1] = 0, 151935
     got = _run(hidden, w_u, rows, targets)
-    pick = sorted({0, 1, len(rows) - 1, *np.random.default_rng(3).integers(0, len(rows), 9)})
+    pick = sorted({1, *[i for k in range(0, len(rows), 32) for i in (k, min(k + 31, len(rows) - 1))]})
     ref = teacher_forced_logprobs(hidden, [rows[i] for i in pick], [targets[i] for i in pick], w_u)
     err = float(np.abs(got[pick] - ref).max())
-    print(f"  {len(rows)} rows, sampled max abs err {err:.2e}", flush=True)
+    print(f"  {len(rows)} rows, {len(pick)} sampled, max abs err {err:.2e}", flush=True)
     assert np.isfinite(got).all() and err <= TOL
     assert (got <= 1e-6).all()  # log-probabilities of a distribution
 
