@@ -43,7 +43,9 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # summed over the call's dispatches (the 27B-like call is a main launch and a merge pass).
 # Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, for
 # the main launch: the share of the cycles the clock actually ran.
-_SHA = "298ccab48f744f83c05610ada361100156ac19a6c809f7f27f6e6363f2c47308"
+# Counted on source 298ccab4…; the source was then changed in host code only (the launcher's
+# per-device CU count), its gfx950 device assembly compared identical, and the key moved on.
+_SHA = "e6df7c348133a046eb2d5fa7a2a2b586910cc5b5a70fc5e7009a1a559a90cb31"
 MEASURED_TRAFFIC = {
     5: (_SHA, 3957665493),
     2: (_SHA, 122489856),

@@ -23,7 +23,8 @@
  *    need scratch memory take it from the caller as a workspace (blink_score_targets, and
  *    blink_prefix_tail_attention where its work split uses one); the variant
  *    blink_score_targets_noalloc uses a fixed static scratch array instead (the one exception
- *    to "no global state", described there).
+ *    to "no global state", described there). The library also remembers each device's
+ *    compute-unit count after first reading it (a property of the hardware, not of a call).
  *  - Device entry points are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream). Device arrays must stay alive until the work on `stream` has finished.
  *  - bf16 means the 16-bit brain-float storage format. All tensors are dense and row-major

@@ -73,6 +73,8 @@
 //    light ones fill in at the end (in a 65536-token causal prefill, 7-9% faster than row
 //    order). The re-cut small units then run first, still one per CU.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -1183,12 +1185,21 @@ int run(Args &a, const void *q, const void *k_tail, const void *v_tail, const vo
   return blink::ok();
 }
 
+// Compute units of the current device. The count is read from the runtime once per device
+// and kept (a property of the hardware, not of any call); a call then costs one hipGetDevice.
 int device_cus(int &cus) {
-  int device = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices] = {};
+  int device = -1;
   cus = 0;
-  if (hipGetDevice(&device) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+  if (hipGetDevice(&device) != hipSuccess || device < 0)
     return blink::fail(BLINK_E_DEVICE, "prefix tail attention: no device");
+  if (device < kMaxDevices) cus = known[device].load(std::memory_order_relaxed);
+  if (cus > 0) return BLINK_OK;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus < 1)
+    return blink::fail(BLINK_E_DEVICE, "prefix tail attention: no device");
+  if (device < kMaxDevices) known[device].store(cus, std::memory_order_relaxed);
   return BLINK_OK;
 }
 

@@ -153,17 +153,14 @@ extern "C" int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_of
       return fail(BLINK_E_INVALID, "option entry %d has token id %d outside [0, %lld)", e,
                   cand_ids[e], (long long)vocab);
 
-  // Per-thread work arrays, reused across calls. Their addresses are taken once: inside a
-  // shared library every access to a thread_local goes through a TLS lookup call.
-  static thread_local std::vector<uint64_t> tl_bits;
-  static thread_local std::vector<int32_t> tl_word_base, tl_col, tl_cursor;
+  // Work arrays of this call (the library keeps nothing between calls): a bitmap of the
+  // vocabulary and per-entry columns, tens of KB at a 151936-row vocabulary.
   const size_t words = size_t((vocab + 63) >> 6);
-  tl_bits.assign(words, 0);
-  tl_word_base.resize(words);
-  tl_col.resize(size_t(total));
-  uint64_t *bits = tl_bits.data();
-  int32_t *word_base = tl_word_base.data();
-  int32_t *col = tl_col.data();
+  std::vector<uint64_t> bits_v(words, 0);
+  std::vector<int32_t> word_base_v(words), col_v(static_cast<size_t>(total));
+  uint64_t *bits = bits_v.data();
+  int32_t *word_base = word_base_v.data();
+  int32_t *col = col_v.data();
   for (int32_t e = 0; e < total; ++e) {
     const uint32_t t = uint32_t(cand_ids[e]);
     bits[t >> 6] |= uint64_t(1) << (t & 63);
@@ -174,8 +171,8 @@ extern "C" int blink_pack_labels(const int32_t *cand_ids, const int32_t *cand_of
     for (uint64_t m = bits[w]; m; m &= m - 1)
       row_id[u++] = int32_t(w * 64 + size_t(__builtin_ctzll(m)));
   }
-  tl_cursor.assign(size_t(u) + 1, 0);
-  int32_t *cursor = tl_cursor.data();
+  std::vector<int32_t> cursor_v(size_t(u) + 1, 0);
+  int32_t *cursor = cursor_v.data();
   for (int32_t e = 0; e < total; ++e) {
     const uint32_t t = uint32_t(cand_ids[e]);
     const uint64_t below = bits[t >> 6] & ((uint64_t(1) << (t & 63)) - 1);
