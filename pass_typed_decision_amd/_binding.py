@@ -315,6 +315,8 @@ def attention_workspace(total_valid_tokens: int, n_heads_q: int, n_heads_kv: int
         int(total_valid_tokens), int(n_heads_q), int(n_heads_kv), int(head_dim), int(prefix_len)))
     if size == 0:
         return None
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
     return torch.empty(size, dtype=torch.uint8, device=device)
 
 

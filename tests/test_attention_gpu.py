@@ -148,6 +148,54 @@ def test_key_split_matches_oracle_whole(name):
     assert err <= ATTN_TOL and gap <= ATTN_TOL
 
 
+def test_workspace_query_matches_the_split_plan():
+    # The library's workspace size is what the key split of the last round needs on this
+    # device (none when it does not split): pieces x KV heads x 12 waves x 64 lanes x
+    # (D / 2 + 2) floats.
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(11)
+    cases = [(10864, 40, 8, 128, 65536), (5338, 32, 8, 128, 2048), (3242, 40, 8, 128, 1500),
+             (6258, 16, 4, 64, 2900), (74705, 32, 8, 128, 0)]
+    for _ in range(200):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        hq = hkv * int(rng.integers(1, 9))
+        cases.append((int(rng.integers(1, 60000)), hq, hkv, int(rng.choice([64, 128])),
+                      int(rng.integers(0, 70000))))
+    for tokens, hq, hkv, d, p in cases:
+        plan = attention_split(tokens * (hq // hkv), hkv, cus, p)
+        ws = blink.attention_workspace(tokens, hq, hkv, d, p)
+        if plan is None:
+            assert ws is None, (tokens, hq, hkv, d, p)
+        else:
+            _, left, ways, _ = plan
+            assert ws is not None and ws.is_cuda
+            assert ws.numel() == left * ways * hkv * 12 * 64 * (d // 2 + 2) * 4
+
+
+def test_undersized_workspace_falls_back_to_the_row_split():
+    # A workspace smaller than the query asks for is not used: the launch keeps the row
+    # re-cut, exactly as with none.
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = SPLIT["ways2_d128"]
+    req = Request(cfg, parts=("q", "k_tail", "v_tail", "k_prefix", "v_prefix"))
+    tokens = int(np.sum(req.tail_len))
+    full = blink.attention_workspace(tokens, cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim,
+                                     cfg.prefix_len)
+    assert full is not None
+    short = torch.zeros(full.numel() - 16, dtype=torch.uint8, device="cuda")
+    got = run_attention(req, workspace=short)
+    plain = run_attention(req, workspace=None)
+    rows = valid_rows(req)
+    np.testing.assert_array_equal(got[rows], plain[rows])
+
+
 # The largest context the boundary accepts (prefix + tail = 131072 tokens): one question whose
 # tail is the whole context with no prefix (2048 tiles of causal tail attention, as when the
 # prefix itself is encoded), and the longest prefix with a one-token tail.
