@@ -68,6 +68,12 @@
 //    the 8 XCDs (dispatch is round-robin over XCDs) streams one head's prefix K/V through its
 //    own L2. The rows left for the last round of workgroups are re-cut into smaller units
 //    (unit_split) so that that round covers every CU.
+//  * Given a caller workspace, when the 384-row units left after the full rounds are few enough
+//    that w >= 2 pieces of each fill one round (split_plan), each of them runs instead as w
+//    pieces over disjoint runs of prefix tiles, only the last piece walking the tail. The
+//    pieces write their FP32 partial sums (O, the row's reference, the row sum) to the
+//    workspace, and a merge pass of the same kernel (one workgroup per split unit and head, no
+//    matrix work) rescales them to their largest reference and adds them.
 //  * Units are dispatched from the last row to the first. A causal row sees one more key than
 //    the row before it, so later units carry more work; starting the heaviest first lets the
 //    light ones fill in at the end (in a 65536-token causal prefill, 7-9% faster than row
