@@ -38,15 +38,13 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
 # rocprofv3 readings of the attention per call, keyed by workload number, with the sha256 of
-# the kernel source they were taken on (a changed kernel reports null until it is counted
-# again). HBM bytes = FETCH_SIZE (x2, calibrated on a plain 1 GiB copy) + WRITE_SIZE (x1),
+# what decides the attention's device code (its two sources and the build script with their
+# flags) at the time they were taken; once any of those changes they read null until counted
+# again. HBM bytes = FETCH_SIZE (x2, calibrated on a plain 1 GiB copy) + WRITE_SIZE (x1),
 # summed over the call's dispatches (the 27B-like call is a main launch and a merge pass).
 # Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, for
 # the main launch: the share of the cycles the clock actually ran.
-# Counted on source 298ccab4…; later changes to that file touched host code and comments only
-# (the launcher's per-device CU count, the design notes), its gfx950 device assembly compared
-# identical each time, and the key moved on with them.
-_SHA = "f121eca947f5667df0b1f2e8c14dc5daa58a8d39b6f8d5327fa6b76968b444a7"
+_SHA = None  # set once the current sources are counted
 MEASURED_TRAFFIC = {
     5: (_SHA, 3957665493),
     2: (_SHA, 122489856),
@@ -59,16 +57,20 @@ MEASURED_MFMA_BUSY = {
     4: (_SHA, 0.119),
     3: (_SHA, 0.582),
 }
-ATTENTION_SOURCE = os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention.hip")
+ATTENTION_SOURCES = [os.path.join(ROOT, "pass_typed_decision_amd", *parts) for parts in (
+    ("csrc", "blink_attention.hip"), ("csrc", "blink_attention_plain.hip"), ("build.py",))]
 
 
 def _source_sha() -> str | None:
     import hashlib
 
-    if not os.path.exists(ATTENTION_SOURCE):
-        return None
-    with open(ATTENTION_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in ATTENTION_SOURCES:
+        if not os.path.exists(path):
+            return None
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _stored(table: dict, number: int):

@@ -83,6 +83,7 @@
 #include <atomic>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "blink_internal.h"
 
@@ -1133,6 +1134,28 @@ hipError_t launch(const Args &a, hipStream_t stream) {
 
 }  // namespace
 
+// The library builds this source twice. The main unit is compiled with an instruction scheduler
+// that favours the matrix-bound launches (every launch with a prefix, and long causal
+// prefills); a second unit, with BLINK_ATTENTION_PLAIN defined, holds only the kernel compiled
+// with the compiler's default scheduler, which measured faster for prefix-free requests of
+// short tails (bound by memory latency, not the matrix pipe). blink_attention_plain_launch runs
+// that second instance for a filled argument block, passed as bytes so that neither unit
+// depends on the other's internal types.
+__attribute__((visibility("hidden"))) hipError_t blink_attention_plain_launch(
+    const void *args, size_t args_bytes, int head_dim, hipStream_t stream);
+
+#ifdef BLINK_ATTENTION_PLAIN
+
+hipError_t blink_attention_plain_launch(const void *args, size_t args_bytes, int head_dim,
+                                        hipStream_t stream) {
+  Args a;
+  if (args_bytes != sizeof(Args)) return hipErrorInvalidValue;
+  memcpy(&a, args, sizeof(Args));
+  return head_dim == 64 ? launch<64>(a, stream) : launch<128>(a, stream);
+}
+
+#else  // the main unit: host code and the library's entry points
+
 namespace {
 
 struct Shape {
@@ -1172,9 +1195,10 @@ int check_shape(const void *q, const void *k_tail, const void *v_tail, const voi
   return BLINK_OK;
 }
 
+// `plain`: launch the second build of the kernel (prefix-free requests of short tails).
 int run(Args &a, const void *q, const void *k_tail, const void *v_tail, const void *k_prefix,
         const void *v_prefix, void *out, const int64_t *d_token_offset,
-        const int32_t *d_valid_start, const Shape &sh, void *stream) {
+        const int32_t *d_valid_start, const Shape &sh, void *stream, bool plain = false) {
   using blink::fail;
   const void *ptrs[] = {q, k_tail, v_tail, out, a.prefix_rows ? k_prefix : q,
                         a.prefix_rows ? v_prefix : q};
@@ -1197,8 +1221,10 @@ int run(Args &a, const void *q, const void *k_tail, const void *v_tail, const vo
   a.scale_log2 = sh.scale * kLog2e;
   if (a.n_units * a.hkv > 0x7fffffffLL) return fail(BLINK_E_LIMIT, "launch too large");
   (void)hipGetLastError();
-  const hipError_t err = sh.head_dim == 64 ? launch<64>(a, static_cast<hipStream_t>(stream))
-                                           : launch<128>(a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err = plain ? blink_attention_plain_launch(&a, sizeof(Args), sh.head_dim, s)
+                         : sh.head_dim == 64 ? launch<64>(a, s)
+                                             : launch<128>(a, s);
   if (err != hipSuccess)
     return fail(BLINK_E_DEVICE, "prefix tail attention launch: %s", hipGetErrorString(err));
   return blink::ok();
@@ -1301,8 +1327,12 @@ extern "C" int blink_prefix_tail_attention(const void *q, const void *k_tail, co
   a.req_unit[1] = a.n_units;
   a.req_pstart[0] = 0;
   a.req_plen[0] = prefix_len;
+  // Prefix-free requests of short tails (under 1024 tokens on average) go to the second build
+  // of the kernel; a long causal prefill stays matrix-bound and stays here.
+  const bool plain = prefix_len == 0 && a.split_first >= a.n_units &&
+                     total_valid_tokens < int64_t(1024) * n_questions;
   return run(a, q, k_tail, v_tail, k_prefix, v_prefix, out, d_token_offset, d_valid_start, sh,
-             stream);
+             stream, plain);
 }
 
 extern "C" int blink_prefix_tail_attention_grouped(
@@ -1375,3 +1405,5 @@ extern "C" int blink_prefix_tail_attention_grouped(
   return run(a, q, k_tail, v_tail, k_prefix, v_prefix, out, d_token_offset, d_valid_start, sh,
              stream);
 }
+
+#endif  // BLINK_ATTENTION_PLAIN

@@ -34,6 +34,7 @@ def checker(tmp_path_factory):
          "-Wno-unused-function", "-Wno-unneeded-internal-declaration",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-o", exe, os.path.join(HERE, "unit_plan_check.hip"),
+         os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_attention_plain.hip"),
          os.path.join(ROOT, "pass_typed_decision_amd", "csrc", "blink_host.cpp")],
         capture_output=True, text=True, timeout=600)
     assert build.returncode == 0, build.stderr[-4000:]
