@@ -44,18 +44,18 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # summed over the call's dispatches (the 27B-like call is a main launch and a merge pass).
 # Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, for
 # the main launch: the share of the cycles the clock actually ran.
-_SHA = None  # set once the current sources are counted
+_SHA = "97de57ae368cdce58586d7c16721e9bdc37299865729064fcc17840598333d40"
 MEASURED_TRAFFIC = {
-    5: (_SHA, 3957665493),
-    2: (_SHA, 122489856),
-    4: (_SHA, 1536939989),
-    3: (_SHA, 1459715115),
+    5: (_SHA, 3939117653),
+    2: (_SHA, 122346795),
+    4: (_SHA, 1536620971),
+    3: (_SHA, 1446226923),
 }
 MEASURED_MFMA_BUSY = {
-    5: (_SHA, 0.609),
-    2: (_SHA, 0.412),
+    5: (_SHA, 0.677),
+    2: (_SHA, 0.448),
     4: (_SHA, 0.119),
-    3: (_SHA, 0.582),
+    3: (_SHA, 0.648),
 }
 ATTENTION_SOURCES = [os.path.join(ROOT, "pass_typed_decision_amd", *parts) for parts in (
     ("csrc", "blink_attention.hip"), ("csrc", "blink_attention_plain.hip"), ("build.py",))]
