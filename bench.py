@@ -40,11 +40,12 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # rocprofv3 readings of the attention per call, keyed by workload number, with the sha256 of
 # what decides the attention's device code (its two sources and the build script with their
 # flags) at the time they were taken; once any of those changes they read null until counted
-# again. HBM bytes = FETCH_SIZE (x2, calibrated on a plain 1 GiB copy) + WRITE_SIZE (x1),
+# again, or until the device assembly of both builds is shown byte-identical to the counted
+# one (a host-only or comment edit), when the key moves to the new sources. HBM bytes = FETCH_SIZE (x2, calibrated on a plain 1 GiB copy) + WRITE_SIZE (x1),
 # summed over the call's dispatches (the 27B-like call is a main launch and a merge pass).
 # Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, for
 # the main launch: the share of the cycles the clock actually ran.
-_SHA = "97de57ae368cdce58586d7c16721e9bdc37299865729064fcc17840598333d40"
+_SHA = "0c83c8613739873b5a62ad2f5433f3f3ddc0987cf35218dbfb3204f3e691c01f"
 MEASURED_TRAFFIC = {
     5: (_SHA, 3939117653),
     2: (_SHA, 122346795),

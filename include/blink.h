@@ -266,10 +266,17 @@ int blink_prefix_tail_attention_grouped(
  *   d_logits    float32 [total_candidates] device output
  *   d_probs     float32 [total_candidates] output
  *   d_argmax    int32 [n] output; -1 (with NaN logits/probs) marks a question whose
- *               table entries were out of range
+ *               table entries were out of range; -1 alone (nothing else written) a question
+ *               whose offsets cannot be used (K_i outside 1..max_options, or past the table)
  *               d_probs and d_argmax are only written, never read: each may be device memory
  *               or pinned host memory the device can access (hipHostMalloc), which the host
  *               may read once the stream has been synchronised.
+ * Launch form, chosen from the sizes and the current device's compute-unit count (read once
+ * per device); every form gives bitwise the same results. Tables of at most 32 MiB of label
+ * rows: one launch, a workgroup per question. Larger tables with n >= 2 x compute units and
+ * max_options * compute units <= 9/8 * total_candidates: one launch, workgroup b taking the
+ * question with the b-th most options (ties by index), so the longest start first. Otherwise
+ * two launches: logits over the flat option list, then one wave per question for the softmax.
  */
 int blink_label_readout(const void *hidden, int64_t hidden_rows, int32_t d_model,
                         const int64_t *d_last_row, const void *w_u, int64_t vocab,

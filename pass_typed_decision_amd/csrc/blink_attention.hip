@@ -80,7 +80,6 @@
 //    order). The re-cut small units then run first, still one per CU.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -1230,28 +1229,10 @@ int run(Args &a, const void *q, const void *k_tail, const void *v_tail, const vo
   return blink::ok();
 }
 
-// Compute units of the current device. The count is read from the runtime once per device
-// and kept (a property of the hardware, not of any call); a call then costs one hipGetDevice.
-int device_cus(int &cus) {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> known[kMaxDevices] = {};
-  int device = -1;
-  cus = 0;
-  if (hipGetDevice(&device) != hipSuccess || device < 0)
-    return blink::fail(BLINK_E_DEVICE, "prefix tail attention: no device");
-  if (device < kMaxDevices) cus = known[device].load(std::memory_order_relaxed);
-  if (cus > 0) return BLINK_OK;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-      cus < 1)
-    return blink::fail(BLINK_E_DEVICE, "prefix tail attention: no device");
-  if (device < kMaxDevices) known[device].store(cus, std::memory_order_relaxed);
-  return BLINK_OK;
-}
-
 // The key-split plan of a single-request launch on the current device, if any; `cus` is set.
 int single_plan(int64_t total_valid_tokens, int32_t n_heads_q, int32_t n_heads_kv,
                 int32_t prefix_len, int &cus, SplitPlan &sp, bool &split) {
-  int rc = device_cus(cus);
+  int rc = blink::device_cus(cus, "prefix tail attention");
   if (rc != BLINK_OK) return rc;
   split = split_plan(total_valid_tokens * (n_heads_q / n_heads_kv), n_heads_kv, cus, prefix_len,
                      sp);
@@ -1389,7 +1370,7 @@ extern "C" int blink_prefix_tail_attention_grouped(
     rows[r] = int64_t(h_valid_start[l] - h_valid_start[f]) * G;
   }
   int cus = 0;
-  if ((rc = device_cus(cus)) != BLINK_OK) return rc;
+  if ((rc = blink::device_cus(cus, "prefix tail attention")) != BLINK_OK) return rc;
   grouped_split(rows, n_requests, n_heads_kv, cus, a.req_full, a.req_small);
   int64_t units = 0;  // the grid and the kernel's unit -> rows map follow the same counts
   for (int r = 0; r < n_requests; ++r) {

@@ -6,10 +6,12 @@
 // of the batch with the newcomer, widest row times row count, stays within the budget and
 // the optional row cap is not reached; otherwise open a new batch. Batch width is its
 // longest row. Batches are laid end to end in one token-major buffer.
+#include <hip/hip_runtime_api.h>
 #include <stdarg.h>
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <numeric>
@@ -34,6 +36,22 @@ int fail(int code, const char *fmt, ...) {
 
 int ok() {
   g_error.clear();
+  return BLINK_OK;
+}
+
+int device_cus(int &cus, const char *who) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices] = {};
+  int device = -1;
+  cus = 0;
+  if (hipGetDevice(&device) != hipSuccess || device < 0)
+    return fail(BLINK_E_DEVICE, "%s: no device", who);
+  if (device < kMaxDevices) cus = known[device].load(std::memory_order_relaxed);
+  if (cus > 0) return BLINK_OK;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus < 1)
+    return fail(BLINK_E_DEVICE, "%s: no device", who);
+  if (device < kMaxDevices) known[device].store(cus, std::memory_order_relaxed);
   return BLINK_OK;
 }
 

@@ -19,7 +19,11 @@
 //  * label_softmax_kernel: one wave per question over its (at most 255) logits: temperature,
 //    max, exp, sum, normalise, and the first index of the largest logit.
 // Small tables (launch-latency-bound) take one launch, label_readout_fused_kernel: one
-// workgroup per question scores its rows and finishes it in the same kernel.
+// workgroup per question scores its rows and finishes it in the same kernel. Large tables of
+// many questions take that kernel in its ranked form instead of the pair: workgroup b takes
+// the question with the b-th most options (every workgroup derives the same order from the
+// offsets), so the longest questions start first and the short ones fill in behind them, and
+// each question's probabilities are written while other workgroups still stream rows.
 // The batched form (blink_label_readout_batched, after _read_batched) replaces the first
 // launch of the streaming path with label_logits_rows_kernel, which reads each distinct label
 // row once however many questions offer it.
@@ -266,26 +270,124 @@ __global__ __launch_bounds__(kThreads) void label_softmax_kernel(
   finish_question(z, K, lane, temperature, lo, false, logits, probs, argmax + i);
 }
 
-// Small option tables (launch latency, not bandwidth, bounds them): one workgroup per
-// question, its waves taking the question's label rows two at a time, wave 0 finishing.
-template <int NCH>
-__global__ __launch_bounds__(kThreads) void label_readout_fused_kernel(
+// The question of rank b (0-based) when questions are ordered by decreasing option count,
+// ties by index (questions with unusable offsets count as 0 options and come last). Every
+// workgroup of the grid computes the same permutation from cand_off, so with one workgroup per
+// rank each question is taken exactly once. One pass over the n <= BLINK_MAX_QUESTIONS
+// questions, one per thread: an LDS histogram of the option counts, a suffix scan of it by
+// wave 0 that names the count K* holding rank b and b's place r among the questions with K*
+// options, then a ballot prefix count over those questions in index order that finds the one
+// at place r. The winning thread also hands over its offsets and hidden row, which saves the
+// workgroup a dependent round trip to memory. Returns i = -1 if no question holds rank b,
+// which only offsets rewritten during the launch can cause.
+struct Ranked {
+  int i;
+  int64_t lo, hi, row;
+};
+
+template <int W>
+__device__ inline Ranked ranked_question(const int32_t *__restrict__ cand_off,
+                                         const int64_t *__restrict__ last_row, int n,
+                                         int64_t total, int max_options, int b) {
+  static_assert(64 * W >= BLINK_MAX_QUESTIONS, "one question per thread");
+  constexpr int kBins = BLINK_MAX_OPTIONS + 1;
+  static_assert(kBins == 256, "wave 0 scans four bins per lane");
+  __shared__ int s_hist[kBins];
+  __shared__ int s_wave[W];
+  __shared__ int s_pick[2];
+  __shared__ Ranked s_won;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  int key = -1;
+  int64_t lo = 0, hi = 0, row = 0;
+  if (t < n) {
+    lo = cand_off[t];
+    hi = cand_off[t + 1];
+    row = last_row[t];
+    key = offsets_usable(lo, hi, total, max_options) ? int(hi - lo) : 0;
+  }
+  for (int k = t; k < kBins; k += 64 * W) s_hist[k] = 0;
+  if (t == 0) {  // stay "none" only if cand_off changed under the launch
+    s_pick[0] = -1;
+    s_won.i = -1;
+  }
+  __syncthreads();
+  if (key >= 0) atomicAdd(&s_hist[key], 1);
+  __syncthreads();
+  if (wave == 0) {
+    // Lane l holds bins 4l..4l+3; `above` counts the questions in bins of higher lanes.
+    int h[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum += h[j] = s_hist[4 * lane + j];
+    int incl = sum;  // inclusive prefix over lanes 0..l
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int above = __shfl(incl, 63) - incl;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (b >= above && b < above + h[j]) {
+        s_pick[0] = 4 * lane + j;
+        s_pick[1] = b - above;
+      }
+      above += h[j];
+    }
+  }
+  __syncthreads();
+  const int want = s_pick[0], place = s_pick[1];
+  const bool mine = key >= 0 && key == want;
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(mine);
+  const int below = __builtin_popcountll(mask & ((uint64_t(1) << lane) - 1));
+  if (lane == 0) s_wave[wave] = __builtin_popcountll(mask);
+  __syncthreads();
+  int before = below;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  if (mine && before == place) s_won = Ranked{t, lo, hi, row};
+  __syncthreads();
+  return s_won;
+}
+
+// One workgroup of W waves per question: its waves take the question's label rows two at a
+// time, wave 0 finishes. RANKED = false: workgroup b takes question b (small option tables,
+// where launch latency, not bandwidth, bounds the readout). RANKED = true: workgroup b takes
+// the question of rank b by decreasing option count, so the dispatcher hands out the longest
+// questions first and the short ones fill in behind them (longest-processing-time-first
+// scheduling), which balances the compute units without splitting a question; used for large
+// tables whose questions outnumber the compute units. The probabilities' writes then overlap
+// other workgroups' row streams instead of waiting for a second launch.
+template <int NCH, int W, bool RANKED>
+__global__ __launch_bounds__(64 * W) void label_readout_fused_kernel(
     const uint16_t *__restrict__ hidden, int64_t hidden_rows, int d_model,
     const int64_t *__restrict__ last_row, const uint16_t *__restrict__ w_u, int64_t vocab,
-    const int32_t *__restrict__ cand_ids, const int32_t *__restrict__ cand_off, int64_t total,
-    int max_options, float temperature, float *__restrict__ logits, float *__restrict__ probs,
-    int32_t *__restrict__ argmax) {
+    const int32_t *__restrict__ cand_ids, const int32_t *__restrict__ cand_off, int n,
+    int64_t total, int max_options, float temperature, float *__restrict__ logits,
+    float *__restrict__ probs, int32_t *__restrict__ argmax) {
   __shared__ float s_z[BLINK_MAX_OPTIONS + 1];
-  const int i = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(int(threadIdx.x >> 6));
-  const int64_t lo = cand_off[i], hi = cand_off[i + 1];
+  int i;
+  int64_t lo, hi, row;
+  if constexpr (RANKED) {
+    const Ranked r = ranked_question<W>(cand_off, last_row, n, total, max_options, blockIdx.x);
+    if (r.i < 0) return;  // uniform: read from LDS
+    i = r.i;
+    lo = r.lo;
+    hi = r.hi;
+    row = r.row;
+  } else {
+    i = blockIdx.x;
+    lo = cand_off[i];
+    hi = cand_off[i + 1];
+    row = last_row[i];
+  }
   if (!offsets_usable(lo, hi, total, max_options)) {  // uniform across the workgroup
     if (threadIdx.x == 0) argmax[i] = -1;
     return;
   }
   const int K = int(hi - lo);
-  const int64_t row = last_row[i];
   const bool h_ok = row >= 0 && row < hidden_rows;
   const uint16_t *hrow = hidden + (h_ok ? row : 0) * int64_t(d_model);
   const int nchunks = d_model >> 3;
@@ -296,8 +398,8 @@ __global__ __launch_bounds__(kThreads) void label_readout_fused_kernel(
     h[c] = u32x4{0u, 0u, 0u, 0u};
     if (ch < nchunks) h[c] = *reinterpret_cast<const u32x4 *>(hrow + ch * 8);
   }
-  for (int k = wave; k < K; k += 2 * kWaves) {  // rows k and k + kWaves
-    const int k2 = k + kWaves;
+  for (int k = wave; k < K; k += 2 * W) {  // rows k and k + W
+    const int k2 = k + W;
     const bool two = k2 < K;
     const int32_t id1 = cand_ids[lo + k];
     const int32_t id2 = two ? cand_ids[lo + k2] : 0;
@@ -365,8 +467,17 @@ struct ReadoutArgs {
 // many options would otherwise serialise on one workgroup each).
 constexpr int64_t kFusedMaxBytes = int64_t(32) << 20;
 
+// Whether a large table takes the ranked one-launch form rather than the streaming pair:
+// every compute unit gets at least two questions, so the longest-first order can pair long
+// questions with short ones, and no question is longer than about one compute unit's share of
+// the rows (max_options <= 9/8 of total / cus; the eighth stands for the second launch the
+// ranked form saves). Both forms give bitwise the same results.
+inline bool ranked_fits(const ReadoutArgs &a, int cus) {
+  return int64_t(a.n) >= 2 * int64_t(cus) && int64_t(a.max_options) * cus * 8 <= a.total * 9;
+}
+
 template <int NCH>
-hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
+hipError_t launch(const ReadoutArgs &a, int cus, hipStream_t stream) {
   if (a.row_id) {
     const int64_t n_blocks = (a.n_rows + kFlatWaves - 1) / kFlatWaves;
     const int64_t grid = (n_blocks + kXcds - 1) / kXcds * kXcds;
@@ -382,10 +493,20 @@ hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
     return hipGetLastError();
   }
   if (a.total * a.d_model * 2 <= kFusedMaxBytes) {
-    hipLaunchKernelGGL(label_readout_fused_kernel<NCH>, dim3(unsigned(a.n)), dim3(kThreads), 0,
-                       stream, a.hidden, a.hidden_rows, a.d_model, a.last_row, a.w_u, a.vocab,
-                       a.ids, a.off, a.total, a.max_options, a.temperature, a.logits, a.probs,
-                       a.argmax);
+    hipLaunchKernelGGL((label_readout_fused_kernel<NCH, kWaves, false>), dim3(unsigned(a.n)),
+                       dim3(kThreads), 0, stream, a.hidden, a.hidden_rows, a.d_model,
+                       a.last_row, a.w_u, a.vocab, a.ids, a.off, a.n, a.total, a.max_options,
+                       a.temperature, a.logits, a.probs, a.argmax);
+    return hipGetLastError();
+  }
+  if (ranked_fits(a, cus)) {
+    // 16 waves while a lane's hidden chunks and two label rows (12 NCH registers) leave room
+    // under the 128 registers of a 1024-thread workgroup; 8 waves beyond.
+    constexpr int W = NCH <= 8 ? 16 : 8;
+    hipLaunchKernelGGL((label_readout_fused_kernel<NCH, W, true>), dim3(unsigned(a.n)),
+                       dim3(64 * W), 0, stream, a.hidden, a.hidden_rows, a.d_model, a.last_row,
+                       a.w_u, a.vocab, a.ids, a.off, a.n, a.total, a.max_options,
+                       a.temperature, a.logits, a.probs, a.argmax);
     return hipGetLastError();
   }
   const int64_t n_blocks = (a.total + kFlatWaves - 1) / kFlatWaves;
@@ -401,7 +522,7 @@ hipError_t launch(const ReadoutArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-typedef hipError_t (*LaunchFn)(const ReadoutArgs &, hipStream_t);
+typedef hipError_t (*LaunchFn)(const ReadoutArgs &, int, hipStream_t);
 
 }  // namespace
 
@@ -438,12 +559,15 @@ int check_common(const void *hidden, int64_t hidden_rows, int32_t d_model,
 }
 
 int run(const ReadoutArgs &a, void *stream) {
+  int cus = 0;
+  const int rc = blink::device_cus(cus, "label readout");
+  if (rc != BLINK_OK) return rc;
   const int nch = (a.d_model / 8 + 63) / 64;  // 16-byte chunks per lane
   static constexpr LaunchFn fns[] = {launch<1>,  launch<2>,  launch<3>,  launch<4>,
                                      launch<5>,  launch<6>,  launch<7>,  launch<8>,
                                      launch<9>,  launch<10>, launch<11>, launch<12>,
                                      launch<13>, launch<14>, launch<15>, launch<16>};
-  const hipError_t err = fns[nch - 1](a, static_cast<hipStream_t>(stream));
+  const hipError_t err = fns[nch - 1](a, cus, static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
     return blink::fail(BLINK_E_DEVICE, "label readout launch: %s", hipGetErrorString(err));
   return blink::ok();

@@ -91,10 +91,11 @@ def run_attention(req, tensors=None, token_offset=None, tail_len=None, workspace
 
 
 def run_readout(req, last_row=None, cand_ids=None, cand_off=None, temperature=None,
-                batched=False, row_tables=None):
+                batched=False, row_tables=None, max_options=None):
     """Runs the readout through the C ABI: blink_label_readout, or with ``batched``
     blink_label_readout_batched over the distinct-row tables of blink_pack_labels (or the
-    given ``row_tables`` = (row_id, row_first, row_entry))."""
+    given ``row_tables`` = (row_id, row_first, row_entry)). ``max_options`` defaults to the
+    table's largest option count."""
     import torch
 
     import pass_typed_decision_amd as blink
@@ -113,7 +114,7 @@ def run_readout(req, last_row=None, cand_ids=None, cand_off=None, temperature=No
     logits = torch.empty(len(ids), dtype=torch.float32, device="cuda")
     probs = torch.empty_like(logits)
     argmax = torch.empty(n, dtype=torch.int32, device="cuda")
-    kmax = int(np.diff(off).max())
+    kmax = int(np.diff(off).max()) if max_options is None else int(max_options)
     if batched:
         if row_tables is None:
             lr = blink.pack_labels(ids, off, cfg.vocab)

@@ -2,7 +2,11 @@
 
 Bar: label probabilities within 1e-4 (max-abs), logits within 1e-4, argmax exact wherever the
 oracle's top-2 gap exceeds 1e-5 (else one of the tied maxima). All five workloads at full
-size, plus edge cases (1 and 255 options, temperature, malformed tables)."""
+size, plus edge cases (1 and 255 options, temperature, malformed tables), and the launch forms
+against one another: small tables take one fused launch; large ones the streaming pair, or,
+when questions number at least twice the compute units and none is longer than about one
+unit's share of the rows (the plain max packing table on a 256-CU part), one ranked launch
+that hands out the longest questions first. The forms give bitwise the same results."""
 
 import numpy as np
 import pytest
@@ -79,9 +83,11 @@ def test_shared_label_table():
     _check(req, logits, probs, arg, ids=ids)
 
 
-@pytest.mark.parametrize("number", [1, 4], ids=["fused", "streaming"])
-def test_malformed_entries_are_flagged(number):
-    cfg = synth.config(number)
+@pytest.mark.parametrize("number,n_questions", [(1, None), (4, None), (4, 300)],
+                         ids=["fused", "ranked", "streaming"])
+def test_malformed_entries_are_flagged(number, n_questions):
+    cfg = synth.config(number) if n_questions is None else synth.config(number,
+                                                                        n_questions=n_questions)
     req = Request(cfg, parts=READOUT_PARTS)
     ids = req.tables.cand_ids.copy()
     ids[req.tables.cand_off[1]] = cfg.vocab + 5  # question 1: id out of range
@@ -102,6 +108,79 @@ def test_malformed_entries_are_flagged(number):
     sub_off = np.concatenate([[0], np.cumsum([off[i + 1] - off[i] for i in good])])
     sub = np.concatenate([np.arange(off[i], off[i + 1]) for i in good])
     check_argmax(z[sub], sub_off, a[good], arg[good])
+
+
+def _read_in_parts(req, ids, off, parts):
+    """The same questions read in `parts` calls of consecutive questions; results joined."""
+    n = len(off) - 1
+    last = np.asarray(req.pack["last_row"], np.int64)
+    out = [[], [], []]
+    for p in range(parts):
+        q0, q1 = n * p // parts, n * (p + 1) // parts
+        got = run_readout(req, last_row=last[q0:q1], cand_ids=ids[off[q0]:off[q1]],
+                          cand_off=(off[q0:q1 + 1] - off[q0]).astype(np.int32))
+        for acc, x in zip(out, got):
+            acc.append(x)
+    return [np.concatenate(x) for x in out]
+
+
+@pytest.mark.parametrize("counts", ["mixed", "equal"])
+def test_ranked_and_streaming_forms_agree_bitwise(counts):
+    # 512 questions read whole (the ranked launch on a 256-CU part) and as two calls of 256
+    # (the streaming pair there): each question's results depend on its own rows only, so
+    # the two must agree bit for bit. "mixed": the workload's 2..255 options (many equal
+    # counts, so the rank's ties by index are exercised); "equal": 200 options everywhere.
+    cfg = synth.config(4)
+    req = Request(cfg, parts=READOUT_PARTS)
+    ids, off = req.tables.cand_ids, req.tables.cand_off
+    if counts == "equal":
+        n = cfg.n_questions
+        rng = np.random.default_rng(21)
+        ids = np.concatenate([rng.choice(cfg.vocab, 200, replace=False)
+                              for _ in range(n)]).astype(np.int32)
+        off = (np.arange(n + 1) * 200).astype(np.int32)
+    assert len(ids) * cfg.d_model * 2 > 32 << 20
+    whole = run_readout(req, cand_ids=ids, cand_off=off)
+    halves = _read_in_parts(req, ids, off, 2)
+    for a, b in zip(whole, halves):
+        np.testing.assert_array_equal(a, b)
+    if counts == "equal":
+        _check(req, *whole, ids=ids, off=off)
+
+
+def test_unusable_offsets_in_a_ranked_launch():
+    # Questions whose offsets cannot be used (more options than max_options, none, or an end
+    # past the table) rank last in the ranked launch, get argmax -1, and every other question
+    # is still read once and matches the oracle.
+    cfg = synth.config(4)
+    req = Request(cfg, parts=READOUT_PARTS)
+    ids = req.tables.cand_ids
+    off = req.tables.cand_off.astype(np.int64).copy()
+    k = np.diff(off)
+    n, total = len(k), int(off[-1])
+    a = int(np.nonzero(k[:-1] + k[1:] > 255)[0][0])
+    off[a + 1] = off[a + 2]  # question a: over 255 options; question a + 1: none
+    b = int(np.nonzero((k[a + 3:-2] + k[a + 4:-1]) <= 255)[0][0]) + a + 3
+    off[b + 1] = off[b]  # question b: none; question b + 1 takes its rows
+    off[n] = total + 1  # question n - 1 ends past the table
+    bad = [a, a + 1, b, n - 1]
+    d_off = off.astype(np.int32)
+    d_off_ok = d_off.copy()
+    d_off_ok[n] = total
+    logits, probs, arg = run_readout(req, cand_off=d_off, max_options=255)
+    assert (arg[bad] == -1).all()
+    good = [i for i in range(n) if i not in bad]
+    last = np.asarray(req.pack["last_row"], np.int64)
+    z, p, o_arg = label_readout(req.tensors["hidden"], last[good], req.tensors["w_u"],
+                                np.concatenate([ids[d_off_ok[i]:d_off_ok[i + 1]] for i in good]),
+                                np.concatenate([[0], np.cumsum([d_off_ok[i + 1] - d_off_ok[i]
+                                                                for i in good])]),
+                                cfg.temperature)
+    sub = np.concatenate([np.arange(d_off_ok[i], d_off_ok[i + 1]) for i in good])
+    assert np.abs(logits[sub] - z).max() <= LOGIT_TOL
+    assert np.abs(probs[sub] - p).max() <= PROB_TOL
+    sub_off = np.concatenate([[0], np.cumsum([d_off_ok[i + 1] - d_off_ok[i] for i in good])])
+    check_argmax(z, sub_off, o_arg, arg[good])
 
 
 def test_rotations_through_the_readout():
