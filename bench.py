@@ -425,6 +425,21 @@ def teacher_forced_scoring(cfg, tables, pk, tensors, stream, score_len: int = 8,
     torch.cuda.synchronize()
     ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
     ev.close()
+    # The library's product of the same shape, logits only (no log-softmax, bf16 logits
+    # written out): W [vocab, d_model] times the scored rows' transpose, both contiguous.
+    h_t = tensors["hidden"][torch.as_tensor(np.asarray(rows, np.int64)).cuda()].t().contiguous()
+    w = tensors["w_u"]
+    ev = TimingEvents(2 * reps, stream)
+    torch.mm(w, h_t)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev.record(2 * i)
+        torch.mm(w, h_t)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    lib_ms = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
+    ev.close()
+    del h_t
     m = len(rows)
     flops = 2.0 * m * cfg.vocab * cfg.d_model
     wbytes = float(cfg.vocab) * cfg.d_model * 2 + m * cfg.d_model * 2
@@ -433,7 +448,12 @@ def teacher_forced_scoring(cfg, tables, pk, tensors, stream, score_len: int = 8,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "hbm_gbps": wbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-            "work_per_call": f"{flops:.4e} FLOP, {wbytes:.4e} B"}
+            "work_per_call": f"{flops:.4e} FLOP, {wbytes:.4e} B",
+            "library_logits_gemm_ms": lib_ms,
+            "library_logits_gemm_hbm_frac": wbytes / (lib_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "frac_of_library_reference": lib_ms / ms,
+            "library_what": "torch.mm(W_U, H^T) bf16, the same shape, logits only; median of "
+                            f"{reps}"}
 
 
 def library_references(stream, reps: int = 10) -> dict:
