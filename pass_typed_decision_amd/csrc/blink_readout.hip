@@ -6,7 +6,9 @@
 // and "answer assembly" section, softmax (divide by the temperature, subtract the maximum,
 // exponentiate, normalise) and answer_for (most probable option, earlier option on ties).
 //
-// Design. Large option tables (bandwidth-bound) take two launches on the caller's stream:
+// Design. Large option tables (bandwidth-bound) whose questions are too few, or too uneven,
+// to balance the compute units one question per workgroup take two launches on the caller's
+// stream:
 //  * label_logits_flat_kernel streams the label rows: the options of all questions form one
 //    flat list (the CSR order of cand_ids) and every wave scores one entry of it, so the work
 //    is spread evenly whatever the mix of option counts (1..255 per question). A wave loads
