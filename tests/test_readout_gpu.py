@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import LOGIT_TOL, PROB_TOL, Request, check_argmax, run_readout
+from helpers import LOGIT_TOL, PROB_TOL, Request, check_argmax, device_bf16, run_readout
 from oracle.readout import label_readout
 
 pytestmark = pytest.mark.gpu
@@ -181,6 +181,32 @@ def test_unusable_offsets_in_a_ranked_launch():
     assert np.abs(probs[sub] - p).max() <= PROB_TOL
     sub_off = np.concatenate([[0], np.cumsum([d_off_ok[i + 1] - d_off_ok[i] for i in good])])
     check_argmax(z, sub_off, o_arg, arg[good])
+
+
+def test_every_question_unusable_in_a_ranked_launch():
+    # Every question's offsets unusable (none with options, the last with them all): all rank
+    # equal at 0 options, every workgroup still finds its own question, and each gets argmax -1
+    # with nothing else written.
+    import torch
+
+    import pass_typed_decision_amd as blink
+
+    cfg = synth.config(4)
+    req = Request(cfg, parts=READOUT_PARTS)
+    ids = req.tables.cand_ids
+    n, total = cfg.n_questions, len(ids)
+    off = np.zeros(n + 1, np.int32)
+    off[n] = total
+    hidden, w_u = device_bf16(req.tensors["hidden"]), device_bf16(req.tensors["w_u"])
+    d_last = torch.as_tensor(np.asarray(req.pack["last_row"], np.int64)).cuda()
+    logits = torch.full((total,), 7.0, device="cuda")
+    probs = torch.full((total,), 7.0, device="cuda")
+    arg = torch.zeros(n, dtype=torch.int32, device="cuda")
+    blink.label_readout(hidden, d_last, w_u, torch.as_tensor(ids).cuda(),
+                        torch.as_tensor(off).cuda(), cfg.temperature, 255, logits, probs, arg)
+    torch.cuda.synchronize()
+    assert (arg.cpu().numpy() == -1).all()
+    assert (logits.cpu().numpy() == 7.0).all() and (probs.cpu().numpy() == 7.0).all()
 
 
 def test_rotations_through_the_readout():
