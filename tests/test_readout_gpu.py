@@ -148,6 +148,34 @@ def test_ranked_and_streaming_forms_agree_bitwise(counts):
         _check(req, *whole, ids=ids, off=off)
 
 
+def test_ranked_form_at_hidden_5120():
+    # The plain max-packing option mix at hidden 5120: the ranked form's 8-wave workgroups (a
+    # 5120-wide row leaves too few registers for 16 waves), bitwise against the streaming pair
+    # and, on the longest and some other questions, against the oracle. Short tails and a
+    # 16384-row vocabulary keep the inputs small; the table is still far above the one-launch
+    # small-table size.
+    cfg = synth.config(4, d_model=5120, vocab=16384)
+    req = Request(cfg, parts=READOUT_PARTS, tail_len=np.full(cfg.n_questions, 8, np.int32))
+    ids, off = req.tables.cand_ids, req.tables.cand_off
+    assert len(ids) * cfg.d_model * 2 > 32 << 20
+    whole = run_readout(req)
+    halves = _read_in_parts(req, ids, off, 2)
+    for a, b in zip(whole, halves):
+        np.testing.assert_array_equal(a, b)
+    k = np.diff(off)
+    pick = sorted(set(np.argsort(-k, kind="stable")[:8].tolist()) | {0, 1, 255, 256, 510, 511})
+    last = np.asarray(req.pack["last_row"], np.int64)
+    sub_ids = np.concatenate([ids[off[i]:off[i + 1]] for i in pick])
+    sub_off = np.concatenate([[0], np.cumsum([k[i] for i in pick])])
+    z, p, o_arg = label_readout(req.tensors["hidden"], last[pick], req.tensors["w_u"], sub_ids,
+                                sub_off, cfg.temperature)
+    sub = np.concatenate([np.arange(off[i], off[i + 1]) for i in pick])
+    logits, probs, arg = whole
+    assert np.abs(logits[sub] - z).max() <= LOGIT_TOL
+    assert np.abs(probs[sub] - p).max() <= PROB_TOL
+    check_argmax(z, sub_off, o_arg, arg[pick])
+
+
 def test_unusable_offsets_in_a_ranked_launch():
     # Questions whose offsets cannot be used (more options than max_options, none, or an end
     # past the table) rank last in the ranked launch, get argmax -1, and every other question
