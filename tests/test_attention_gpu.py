@@ -31,6 +31,8 @@ SMALL = {
                                tail_lo=1, tail_hi=40),
     "d128_group8": synth.config(2, n_heads_q=16, n_heads_kv=2, prefix_len=90, n_questions=5,
                                 tail_lo=20, tail_hi=90),
+    # No prefix at head_dim 64: the second build of the kernel (prefix-free short tails).
+    "plain_d64": synth.config(1, prefix_len=0, n_questions=12, tail_lo=1, tail_hi=90),
 }
 
 
