@@ -222,7 +222,8 @@ size_t blink_prefix_tail_attention_workspace(int64_t total_valid_tokens, int32_t
  * of the "public entry point" section: the questions of several requests share the forwards
  * of one call). Every question attends to its own request's prefix exactly as in
  * blink_prefix_tail_attention; results are bitwise those of one blink_prefix_tail_attention
- * call per request. The requests' questions are laid out one request after another.
+ * call per request made without a workspace (with one, that call's key-split rows differ by
+ * rounding). The requests' questions are laid out one request after another.
  *
  *   q, k_tail, v_tail, out, d_token_offset, d_valid_start: as in blink_prefix_tail_attention,
  *                     over the questions of every request (1..512 questions in total)
